@@ -1,0 +1,163 @@
+"""Paged MLA decode on MI355X (gfx950): Python binding of libmla_decode.so.
+
+Two calls, as a serving engine makes them (the PAI FlashMLA tutorial on
+segmentfault, "云上玩转DeepSeek系列之五", section 二.2: metadata once per decode
+step, the forward once per layer):
+
+    tile_md, num_splits = get_mla_metadata(cache_seqlens, s_q * h_q, h_kv)
+    out, lse = mla_decode_with_kvcache(q, blocked_k, block_table, cache_seqlens,
+                                       dv, softmax_scale, causal,
+                                       metadata=(tile_md, num_splits))
+
+This module only marshals arguments: torch provides device memory and the
+current stream, and every step of the computation runs in the library's HIP
+kernels.  Importing it does not load the library; the first call does, and
+raises if the library has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import MLAError, TILE_MD_INTS
+
+__all__ = ["get_mla_metadata", "mla_decode_with_kvcache", "plan_host", "default_num_parts",
+           "workspace_size", "MLAError", "TILE_MD_INTS"]
+
+D_QK = 576
+D_V = 512
+BLOCK_SIZE = 64
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def default_num_parts(q_rows: int, h_kv: int = 1, device: int = 0) -> int:
+    n = ctypes.c_int32(0)
+    _lib.check(_lib.load().mla_default_num_parts(int(device), int(q_rows), int(h_kv),
+                                                 ctypes.byref(n)), "mla_default_num_parts")
+    return n.value
+
+
+def workspace_size(batch: int, s_q: int, h_q: int, h_kv: int = 1, dv: int = D_V,
+                   num_parts: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    _lib.check(_lib.load().mla_workspace_size(batch, s_q, h_q, h_kv, dv, num_parts, ctypes.byref(n)),
+               "mla_workspace_size")
+    return n.value
+
+
+def plan_host(cache_seqlens, q_rows: int, h_kv: int, num_parts: int):
+    """The plan computed on the host (int32 CPU tensors), identical to get_mla_metadata's."""
+    sl = torch.as_tensor(cache_seqlens, dtype=torch.int32).contiguous().cpu()
+    b = sl.numel()
+    md = torch.empty((num_parts, TILE_MD_INTS), dtype=torch.int32)
+    ns = torch.empty((b + 1,), dtype=torch.int32)
+    _lib.check(_lib.load().mla_plan_host(_ptr(sl) if b else None, b, int(q_rows), int(h_kv),
+                                         int(num_parts), _ptr(md), _ptr(ns)), "mla_plan_host")
+    return md, ns
+
+
+def get_mla_metadata(cache_seqlens: torch.Tensor, q_rows: int, h_kv: int,
+                     num_parts: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Plan the split-KV work for one decode step (enqueued on the current stream).
+
+    cache_seqlens: int32 [b] on the GPU; q_rows = s_q * h_q.
+    Returns (tile_md int32 [num_parts, 8], num_splits int32 [b + 1]) on the same device.
+    """
+    if cache_seqlens.dtype != torch.int32 or not cache_seqlens.is_cuda:
+        raise ValueError("cache_seqlens must be an int32 GPU tensor")
+    sl = cache_seqlens.contiguous()
+    dev = sl.device
+    if num_parts is None:
+        num_parts = default_num_parts(q_rows, h_kv, dev.index or 0)
+    b = sl.numel()
+    md = torch.empty((num_parts, TILE_MD_INTS), dtype=torch.int32, device=dev)
+    ns = torch.empty((b + 1,), dtype=torch.int32, device=dev)
+    _lib.check(_lib.load().mla_get_metadata(_ptr(sl), b, int(q_rows), int(h_kv), int(num_parts),
+                                            _ptr(md), _ptr(ns), _stream(dev)), "mla_get_metadata")
+    return md, ns
+
+
+def mla_decode_with_kvcache(q: torch.Tensor, blocked_k: torch.Tensor, block_table: torch.Tensor,
+                            cache_seqlens: torch.Tensor, dv: int, softmax_scale: float,
+                            causal: bool, *, metadata=None, num_parts: Optional[int] = None,
+                            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                            workspace: Optional[torch.Tensor] = None):
+    """Paged MLA decode.
+
+    q           bf16 [b, s_q, h_q, 576], last dim contiguous
+    blocked_k   bf16 [num_blocks, 64, h_kv, 576] (any strided view with unit last-dim
+                stride, e.g. the first 576 elements of a [num_blocks, 64, h_kv, 640] cache)
+    block_table int32 [b, max_blocks_per_seq]
+    cache_seqlens int32 [b]
+    metadata    optional (tile_md, num_splits) from get_mla_metadata for these seqlens
+    Returns (out bf16 [b, s_q, h_q, dv], lse fp32 [b, s_q, h_q]).
+    """
+    if q.dim() != 4 or blocked_k.dim() != 4 or block_table.dim() != 2:
+        raise ValueError("q and blocked_k must be 4-D, block_table 2-D")
+    if q.dtype != torch.bfloat16 or blocked_k.dtype != torch.bfloat16:
+        raise ValueError("q and blocked_k must be bfloat16")
+    if block_table.dtype != torch.int32 or cache_seqlens.dtype != torch.int32:
+        raise ValueError("block_table and cache_seqlens must be int32")
+    dev = q.device
+    for t in (q, blocked_k, block_table, cache_seqlens):
+        if not t.is_cuda or t.device != dev:
+            raise ValueError("all tensors must be on the same GPU")
+    if q.stride(-1) != 1 or blocked_k.stride(-1) != 1 or block_table.stride(-1) != 1:
+        raise ValueError("the last dimension of q, blocked_k and block_table must be contiguous")
+    b, s_q, h_q, d = q.shape
+    num_blocks, block_size, h_kv, dk = blocked_k.shape
+    if dk != d:
+        raise ValueError("q and blocked_k disagree on the head size")
+    if block_table.shape[0] != b or cache_seqlens.numel() != b:
+        raise ValueError("block_table / cache_seqlens batch mismatch")
+    seqlens = cache_seqlens.contiguous()
+    if out is None:
+        out = torch.empty((b, s_q, h_q, dv), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((b, s_q, h_q), dtype=torch.float32, device=dev)
+    tile_md = num_splits = None
+    if metadata is not None:
+        tile_md, num_splits = metadata
+        num_parts = tile_md.shape[0]
+    parts = 0 if num_parts is None else int(num_parts)
+    need = workspace_size(b, s_q, h_q, h_kv, dv, parts) if b else 256
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
+    p = _lib.DecodeParams()
+    p.q = q.data_ptr()
+    p.q_batch_stride, p.q_seq_stride, p.q_head_stride = q.stride(0), q.stride(1), q.stride(2)
+    p.batch, p.s_q, p.h_q = b, s_q, h_q
+    p.k_cache = blocked_k.data_ptr()
+    p.k_block_stride, p.k_row_stride, p.k_head_stride = (blocked_k.stride(0), blocked_k.stride(1),
+                                                         blocked_k.stride(2))
+    p.num_blocks, p.block_size, p.h_kv, p.d = num_blocks, block_size, h_kv, d
+    p.block_table = block_table.data_ptr()
+    p.block_table_stride = block_table.stride(0)
+    p.max_blocks_per_seq = block_table.shape[1]
+    p.cache_seqlens = seqlens.data_ptr()
+    p.dv = int(dv)
+    p.softmax_scale = float(softmax_scale)
+    p.causal = 1 if causal else 0
+    p.tile_md = None if tile_md is None else tile_md.data_ptr()
+    p.num_splits = None if num_splits is None else num_splits.data_ptr()
+    p.num_parts = parts
+    p.workspace = workspace.data_ptr()
+    p.workspace_bytes = workspace.numel()
+    p.out = out.data_ptr()
+    p.out_batch_stride, p.out_seq_stride, p.out_head_stride = out.stride(0), out.stride(1), out.stride(2)
+    p.lse = lse.data_ptr()
+    p.lse_batch_stride, p.lse_seq_stride, p.lse_head_stride = lse.stride(0), lse.stride(1), lse.stride(2)
+    _lib.check(_lib.load().mla_decode_with_kvcache(ctypes.byref(p), _stream(dev)),
+               "mla_decode_with_kvcache")
+    return out, lse

@@ -1,0 +1,66 @@
+"""Compile the HIP library libmla_decode.so in-tree for gfx950.
+
+Usage: python -m paged_mla_decode_04_amd.build   (or __graft_entry__.build()).
+hipcc cross-compiles the device code without a GPU present.
+"""
+
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB_NAME = "libmla_decode.so"
+LIB_PATH = os.path.join(HERE, LIB_NAME)
+SOURCES = ["mla_api.hip", "mla_kernels.hip"]
+ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
+
+HIPCC_FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    # keep hipcc from forming packed fp32 ops on its own
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-command-line-argument",
+]
+
+
+def hipcc() -> str:
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    return os.path.join(rocm, "bin", "hipcc")
+
+
+def build(verbose: bool = False) -> str:
+    objs = []
+    procs = []
+    for src in SOURCES:
+        obj = os.path.join(CSRC, src.replace(".hip", ".o"))
+        cmd = [hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+        objs.append(obj)
+    failed = []
+    for src, p in procs:
+        out, _ = p.communicate()
+        text = out.decode(errors="replace")
+        text = "\n".join(l for l in text.splitlines() if "packed-fp32-ops" not in l)
+        if p.returncode != 0:
+            failed.append(f"{src}:\n{text}")
+        elif verbose and text.strip():
+            print(text)
+    if failed:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(failed))
+    tmp = LIB_PATH + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stdout.decode(errors="replace"))
+    os.replace(tmp, LIB_PATH)
+    for o in objs:
+        os.remove(o)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

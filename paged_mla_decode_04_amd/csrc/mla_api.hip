@@ -1,0 +1,221 @@
+// C ABI of the paged MLA decode library: argument checks, workspace layout and
+// launches on the caller's stream.  The operation and the error rules are
+// documented in include/mla_decode.h.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include "../../include/mla_decode.h"
+#include "mla_internal.h"
+#include "mla_plan.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+int cu_count(int device) {
+  if (device < 0 || device >= kMaxDevices) return 0;
+  int v = g_cu_count[device].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int c = 0;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || c <= 0) return 0;
+  g_cu_count[device].store(c, std::memory_order_relaxed);
+  return c;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct WorkspaceLayout {
+  size_t tile_md, num_splits, part_lse, part_o, total;
+};
+
+WorkspaceLayout layout(int64_t batch, int64_t rows, int64_t dv, int64_t num_parts) {
+  WorkspaceLayout w;
+  const int64_t slots = batch + num_parts;
+  w.tile_md = 0;
+  w.num_splits = align256((size_t)num_parts * mla::kTileMdInts * 4);
+  w.part_lse = w.num_splits + align256((size_t)(batch + 1) * 4);
+  w.part_o = w.part_lse + align256((size_t)(slots * rows) * 4);
+  w.total = w.part_o + align256((size_t)(slots * rows * dv) * 4);
+  return w;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+int default_parts(int device, int rows) {
+  const int cus = cu_count(device);
+  if (cus <= 0) return -1;
+  const int per = cus / mla::row_blocks(rows);
+  return per < 1 ? 1 : per;
+}
+
+int check_plan_args(int32_t batch, int32_t q_rows, int32_t h_kv, int32_t num_parts) {
+  if (batch < 0 || q_rows <= 0 || h_kv <= 0 || num_parts <= 0) return MLA_ERR_BAD_SHAPE;
+  if (q_rows % h_kv) return MLA_ERR_BAD_SHAPE;
+  if (q_rows / h_kv > MLA_MAX_ROWS) return MLA_ERR_UNSUPPORTED;
+  if (num_parts > (1 << 20)) return MLA_ERR_BAD_SHAPE;
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case MLA_ERR_BAD_SHAPE: return "invalid or inconsistent size";
+    case MLA_ERR_BAD_STRIDE: return "stride or alignment not supported";
+    case MLA_ERR_UNSUPPORTED: return "unsupported configuration (needs d=576, dv=512, block_size=64, h_kv=1)";
+    case MLA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MLA_ERR_HIP: return "HIP runtime error";
+    case MLA_ERR_BAD_ARGUMENT: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+size_t mla_decode_params_size(void) { return sizeof(mla_decode_params); }
+
+int mla_default_num_parts(int device, int32_t q_rows, int32_t h_kv, int32_t* num_parts) {
+  if (!num_parts) return MLA_ERR_NULL_POINTER;
+  if (q_rows <= 0 || h_kv <= 0 || q_rows % h_kv) return MLA_ERR_BAD_SHAPE;
+  const int p = default_parts(device, q_rows / h_kv);
+  if (p < 0) return MLA_ERR_HIP;
+  *num_parts = p;
+  return MLA_OK;
+}
+
+int mla_plan_host(const int32_t* cache_seqlens_h, int32_t batch, int32_t q_rows, int32_t h_kv,
+                  int32_t num_parts, int32_t* tile_md_h, int32_t* num_splits_h) {
+  if ((!cache_seqlens_h && batch > 0) || !tile_md_h || !num_splits_h) return MLA_ERR_NULL_POINTER;
+  const int st = check_plan_args(batch, q_rows, h_kv, num_parts);
+  if (st != MLA_OK) return st;
+  mla::plan_split_kv(cache_seqlens_h, batch, q_rows / h_kv, num_parts, tile_md_h, num_splits_h);
+  return MLA_OK;
+}
+
+int mla_get_metadata(const int32_t* cache_seqlens_d, int32_t batch, int32_t q_rows, int32_t h_kv,
+                     int32_t num_parts, int32_t* tile_md_d, int32_t* num_splits_d, void* stream) {
+  if ((!cache_seqlens_d && batch > 0) || !tile_md_d || !num_splits_d) return MLA_ERR_NULL_POINTER;
+  const int st = check_plan_args(batch, q_rows, h_kv, num_parts);
+  if (st != MLA_OK) return st;
+  if (mla::launch_plan(cache_seqlens_d, batch, q_rows / h_kv, num_parts, tile_md_d, num_splits_d,
+                       (hipStream_t)stream) != hipSuccess)
+    return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+int mla_workspace_size(int32_t batch, int32_t s_q, int32_t h_q, int32_t h_kv, int32_t dv,
+                       int32_t num_parts, size_t* bytes) {
+  if (!bytes) return MLA_ERR_NULL_POINTER;
+  if (batch < 0 || s_q <= 0 || h_q <= 0 || h_kv <= 0 || dv <= 0 || h_q % h_kv) return MLA_ERR_BAD_SHAPE;
+  const int64_t rows = (int64_t)s_q * h_q / h_kv;
+  if (rows > MLA_MAX_ROWS) return MLA_ERR_UNSUPPORTED;
+  if (num_parts <= 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+    num_parts = default_parts(dev, (int)rows);
+    if (num_parts < 0) return MLA_ERR_HIP;
+  }
+  *bytes = layout(batch, rows, dv, num_parts).total;
+  return MLA_OK;
+}
+
+int mla_decode_with_kvcache(const mla_decode_params* p, void* stream) {
+  if (!p) return MLA_ERR_NULL_POINTER;
+  if (p->batch < 0 || p->s_q <= 0 || p->h_q <= 0 || p->h_kv <= 0 || p->num_blocks < 0 ||
+      p->max_blocks_per_seq < 0 || p->block_size <= 0 || p->d <= 0 || p->dv <= 0)
+    return MLA_ERR_BAD_SHAPE;
+  if (p->d != 576 || p->dv != 512 || p->block_size != 64 || p->h_kv != 1) return MLA_ERR_UNSUPPORTED;
+  if (p->h_q % p->h_kv) return MLA_ERR_BAD_SHAPE;
+  const int64_t rows = (int64_t)p->s_q * p->h_q / p->h_kv;
+  if (rows > MLA_MAX_ROWS) return MLA_ERR_UNSUPPORTED;
+  if (!(p->softmax_scale == p->softmax_scale) || isinf(p->softmax_scale)) return MLA_ERR_BAD_ARGUMENT;
+  if (p->batch == 0) return MLA_OK;
+  if (!p->q || !p->k_cache || !p->block_table || !p->cache_seqlens || !p->out || !p->lse || !p->workspace)
+    return MLA_ERR_NULL_POINTER;
+  if ((p->tile_md == nullptr) != (p->num_splits == nullptr)) return MLA_ERR_NULL_POINTER;
+  // strides and alignment (elements; 16-byte vector loads and stores)
+  if (!aligned16(p->q) || !aligned16(p->k_cache) || !aligned16(p->out)) return MLA_ERR_BAD_STRIDE;
+  if (((uintptr_t)p->workspace & 255) != 0) return MLA_ERR_BAD_STRIDE;
+  if (p->q_batch_stride % 8 || p->q_seq_stride % 8 || p->q_head_stride % 8) return MLA_ERR_BAD_STRIDE;
+  if (p->out_batch_stride % 8 || p->out_seq_stride % 8 || p->out_head_stride % 8) return MLA_ERR_BAD_STRIDE;
+  if (p->k_block_stride % 8 || p->k_row_stride % 8 || p->k_row_stride < p->d) return MLA_ERR_BAD_STRIDE;
+  if (p->k_block_stride < 0 || p->q_batch_stride < 0 || p->q_seq_stride < 0 || p->q_head_stride < 0 ||
+      p->out_batch_stride < 0 || p->out_seq_stride < 0 || p->out_head_stride < 0 ||
+      p->lse_batch_stride < 0 || p->lse_seq_stride < 0 || p->lse_head_stride < 0)
+    return MLA_ERR_BAD_STRIDE;
+  if (p->block_table_stride < p->max_blocks_per_seq) return MLA_ERR_BAD_STRIDE;
+  if ((int64_t)64 * p->k_row_stride * 2 > INT32_MAX) return MLA_ERR_BAD_STRIDE;
+  if ((int64_t)p->max_blocks_per_seq * 64 > INT32_MAX) return MLA_ERR_BAD_SHAPE;
+
+  int num_parts = p->num_parts;
+  if (p->tile_md) {
+    if (num_parts <= 0) return MLA_ERR_BAD_SHAPE;
+  } else if (num_parts <= 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+    num_parts = default_parts(dev, (int)rows);
+    if (num_parts < 0) return MLA_ERR_HIP;
+  }
+  if (num_parts > (1 << 20)) return MLA_ERR_BAD_SHAPE;
+  const WorkspaceLayout w = layout(p->batch, rows, p->dv, num_parts);
+  if (p->workspace_bytes < w.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* ws = (uint8_t*)p->workspace;
+  const int32_t* tile_md = p->tile_md;
+  const int32_t* num_splits = p->num_splits;
+  if (!tile_md) {
+    int32_t* md = (int32_t*)(ws + w.tile_md);
+    int32_t* ns = (int32_t*)(ws + w.num_splits);
+    if (mla::launch_plan(p->cache_seqlens, p->batch, (int)rows, num_parts, md, ns, s) != hipSuccess)
+      return MLA_ERR_HIP;
+    tile_md = md;
+    num_splits = ns;
+  }
+
+  mla::DecodeArgs a;
+  a.q = (const uint16_t*)p->q;
+  a.q_sb = p->q_batch_stride;
+  a.q_ss = p->q_seq_stride;
+  a.q_sh = p->q_head_stride;
+  a.k = (const uint8_t*)p->k_cache;
+  a.k_block_bytes = p->k_block_stride * 2;
+  a.k_row_bytes = p->k_row_stride * 2;
+  a.num_blocks = p->num_blocks;
+  a.block_table = p->block_table;
+  a.bt_stride = p->block_table_stride;
+  a.max_blocks = p->max_blocks_per_seq;
+  a.seqlens = p->cache_seqlens;
+  a.batch = p->batch;
+  a.s_q = p->s_q;
+  a.h_q = p->h_q;
+  a.rows = (int32_t)rows;
+  a.causal = p->causal ? 1 : 0;
+  a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  a.tile_md = tile_md;
+  a.num_splits = num_splits;
+  a.num_parts = num_parts;
+  a.row_blocks = mla::row_blocks((int)rows);
+  a.part_lse = (float*)(ws + w.part_lse);
+  a.part_o = (float*)(ws + w.part_o);
+  a.out = (uint16_t*)p->out;
+  a.o_sb = p->out_batch_stride;
+  a.o_ss = p->out_seq_stride;
+  a.o_sh = p->out_head_stride;
+  a.lse = p->lse;
+  a.l_sb = p->lse_batch_stride;
+  a.l_ss = p->lse_seq_stride;
+  a.l_sh = p->lse_head_stride;
+
+  if (mla::launch_decode(a, s) != hipSuccess) return MLA_ERR_HIP;
+  if (mla::launch_combine(a, s) != hipSuccess) return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+}  // extern "C"

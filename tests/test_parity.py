@@ -1,0 +1,201 @@
+"""GPU parity: the HIP path against the fp64 CPU oracle.
+
+Tolerance, elementwise: |out - ref| <= 1e-2 * max(1, |ref|) and, on rows with
+a visible key, |lse - ref| <= 2e-3; a row with no visible key must give
+out = 0 and lse = -inf on both sides.
+
+Full-size workloads run in the launch configuration the benchmark times
+(default number of parts, plan from get_mla_metadata) and are compared on
+sampled sequences the oracle computes one by one, plus finiteness of every
+output.  Small cases span several pages with ragged tails, both entry pitches,
+causal and not, with every cache byte the result must not depend on poisoned
+with NaN.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import bits
+from oracle import mla_ref
+from paged_mla_decode_04_amd import (get_mla_metadata, mla_decode_with_kvcache, plan_host,
+                                     default_num_parts)
+from paged_mla_decode_04_amd.workloads import D_V, WORKLOADS, Workload, draw
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 1e-2
+LSE_TOL = 2e-3
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(inp, num_parts=None, use_metadata=True, dev="cuda:0"):
+    g = inp.to(dev)
+    w = inp.workload
+    meta = None
+    if use_metadata:
+        meta = get_mla_metadata(g.cache_seqlens, w.s_q * w.h_q, w.h_kv, num_parts=num_parts)
+    out, lse = mla_decode_with_kvcache(g.q, g.blocked_k, g.block_table, g.cache_seqlens, D_V,
+                                       w.softmax_scale, w.causal, metadata=meta,
+                                       num_parts=num_parts)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu(), meta
+
+
+def oracle(inp, batch_indices=None):
+    return mla_ref.mla_decode_ref(bits(inp.q), bits(inp.k_storage), inp.block_table.numpy(),
+                                  inp.cache_seqlens.numpy(), inp.softmax_scale, inp.causal,
+                                  batch_indices=batch_indices)
+
+
+def assert_parity(out, lse, ref_out, ref_lse, rows=None, what=""):
+    o = out.float().numpy().astype(np.float64)
+    l = lse.numpy().astype(np.float64)
+    if rows is not None:
+        o, l, ref_out, ref_lse = o[rows], l[rows], ref_out[rows], ref_lse[rows]
+    empty = np.isneginf(ref_lse)
+    assert np.array_equal(np.isneginf(l), empty), f"{what}: -inf rows differ"
+    assert np.all(o[empty] == 0), f"{what}: empty rows must be 0"
+    full = ~empty
+    d = np.abs(o[full] - ref_out[full])
+    bound = OUT_TOL * np.maximum(1.0, np.abs(ref_out[full]))
+    worst = float(np.max(d / bound)) if d.size else 0.0
+    assert np.all(d <= bound), f"{what}: out error {float(d.max()):.3e} (x{worst:.2f} of bound)"
+    dl = np.abs(l[full] - ref_lse[full])
+    assert np.all(dl <= LSE_TOL), f"{what}: lse error {float(dl.max()):.3e}"
+    return worst
+
+
+def sample_sequences(seqlens, k, seed=0):
+    s = seqlens.tolist()
+    order = np.argsort(s)
+    pick = {int(order[0]), int(order[-1])}
+    rng = np.random.default_rng(seed)
+    while len(pick) < min(k, len(s)):
+        pick.add(int(rng.integers(len(s))))
+    return sorted(pick)
+
+
+@pytest.mark.parametrize("name,k", [("tiny", 2), ("v2lite", 6), ("wide", 4), ("mtp", 3),
+                                    ("skewed", 16)])
+def test_workload_parity(name, k):
+    note(f"[parity] workload {name}: drawing inputs")
+    inp = draw(name)
+    note(f"[parity] workload {name}: GPU decode, b={inp.workload.batch}")
+    out, lse, meta = run_gpu(inp)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    seqs = sample_sequences(inp.cache_seqlens, k)
+    note(f"[parity] workload {name}: oracle on sequences {seqs}")
+    ref_out, ref_lse = oracle(inp, seqs)
+    worst = assert_parity(out, lse, ref_out, ref_lse, rows=seqs, what=name)
+    note(f"[parity] workload {name}: worst out error {worst:.3f} of the bound")
+
+
+SMALL = [
+    # (seqlens, s_q, h_q, causal, pitch, parts)
+    ((37, 130), 1, 16, False, 576, None),
+    ((1, 64, 65, 200), 2, 16, True, 640, 5),
+    ((300, 7, 129), 1, 128, False, 576, 3),
+    ((513, 64, 2), 2, 128, True, 640, 7),
+    ((100, 250), 1, 40, False, 640, 2),
+    ((90, 33, 1000), 2, 64, True, 576, 4),
+    ((77,), 1, 1, False, 576, 1),
+    ((640, 17), 2, 8, True, 576, 9),
+    ((129, 300, 64, 5), 1, 256, False, 576, 6),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"small{i}" for i in range(len(SMALL))])
+def test_small_cases_with_poisoned_cache(case):
+    lens, s_q, h_q, causal, pitch, parts = case
+    w = Workload("small", batch=len(lens), s_q=s_q, h_q=h_q, causal=causal, seqlens="fixed",
+                 fixed_seqlens=lens, pitch=pitch)
+    inp = draw(w, seed=len(lens) * 1000 + h_q, poison=True)
+    note(f"[parity] small {case}")
+    out, lse, _ = run_gpu(inp, num_parts=parts)
+    ref_out, ref_lse = oracle(inp)
+    assert_parity(out, lse, ref_out, ref_lse, what=str(case))
+
+
+def test_empty_and_edge_lengths():
+    lens = (0, 1, 63, 64, 65, 127, 128, 129)
+    w = Workload("edge", batch=len(lens), s_q=2, h_q=16, causal=True, seqlens="fixed",
+                 fixed_seqlens=lens, pitch=640)
+    inp = draw(w, seed=5, poison=True)
+    note("[parity] edge lengths")
+    out, lse, _ = run_gpu(inp, num_parts=3)
+    ref_out, ref_lse = oracle(inp)
+    assert np.isneginf(ref_lse[0]).all() and np.isneginf(ref_lse[1, 0]).all()
+    assert_parity(out, lse, ref_out, ref_lse, what="edge")
+
+
+@pytest.mark.parametrize("parts", [1, 7, 64, 256, 1024])
+def test_split_count_invariance(parts):
+    w = Workload("split", batch=3, s_q=2, h_q=128, causal=True, seqlens="fixed",
+                 fixed_seqlens=(3000, 70, 1500))
+    inp = draw(w, seed=2)
+    note(f"[parity] forced parts {parts}")
+    out, lse, _ = run_gpu(inp, num_parts=parts)
+    ref_out, ref_lse = oracle(inp)
+    assert_parity(out, lse, ref_out, ref_lse, what=f"parts={parts}")
+
+
+def test_internal_plan_equals_explicit_plan():
+    inp = draw("tiny")
+    a = run_gpu(inp, num_parts=5, use_metadata=False)
+    b = run_gpu(inp, num_parts=5, use_metadata=True)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_device_plan_equals_host_plan():
+    for name in ("tiny", "v2lite", "skewed"):
+        inp = draw(name)
+        w = inp.workload
+        rows = w.s_q * w.h_q
+        parts = default_num_parts(rows)
+        md, ns = get_mla_metadata(inp.cache_seqlens.cuda(), rows, 1, num_parts=parts)
+        hmd, hns = plan_host(inp.cache_seqlens, rows, 1, parts)
+        assert torch.equal(md.cpu(), hmd) and torch.equal(ns.cpu(), hns), name
+
+
+def test_page_permutation_is_bit_identical():
+    w = Workload("perm", batch=3, s_q=2, h_q=64, causal=True, seqlens="fixed",
+                 fixed_seqlens=(700, 64, 333))
+    inp = draw(w, seed=4)
+    a_out, a_lse, _ = run_gpu(inp, num_parts=4)
+    nb = inp.k_storage.shape[0]
+    perm = torch.randperm(nb, generator=torch.Generator().manual_seed(9))
+    moved = inp.k_storage.clone()
+    moved[perm] = inp.k_storage
+    inp.k_storage = moved
+    inp.blocked_k = moved[..., :576]
+    inp.block_table = perm[inp.block_table.long()].to(torch.int32)
+    b_out, b_lse, _ = run_gpu(inp, num_parts=4)
+    assert torch.equal(a_out, b_out) and torch.equal(a_lse, b_lse)
+
+
+def test_pitch_640_is_bit_identical_to_576():
+    w = Workload("pitch", batch=2, s_q=1, h_q=128, causal=False, seqlens="fixed",
+                 fixed_seqlens=(1000, 129))
+    inp = draw(w, seed=6)
+    a_out, a_lse, _ = run_gpu(inp, num_parts=3)
+    padded = torch.full(inp.k_storage.shape[:-1] + (640,), float("nan"), dtype=torch.bfloat16)
+    padded[..., :576] = inp.k_storage
+    inp.k_storage = padded
+    inp.blocked_k = padded[..., :576]
+    b_out, b_lse, _ = run_gpu(inp, num_parts=3)
+    assert torch.equal(a_out, b_out) and torch.equal(a_lse, b_lse)
+
+
+def test_results_are_deterministic():
+    inp = draw("v2lite")
+    a = run_gpu(inp)
+    b = run_gpu(inp)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])

@@ -1,0 +1,135 @@
+"""Invariants of the split-KV plan (host mirror; the GPU plan must equal it).
+
+A plan is valid when, over the flattened (sequence, page) order with one
+(possibly empty) unit for a sequence of no tokens, the parts cover every unit
+exactly once, in order, as contiguous ranges; num_splits holds the prefix sums
+of the number of parts touching each sequence; and each part's first-sequence
+split index counts the earlier parts touching that sequence.  Plans are not
+unique -- any such cover is correct -- so the balance is checked as a bound.
+"""
+
+import random
+
+import pytest
+import torch
+
+from paged_mla_decode_04_amd import _lib, plan_host
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib():
+    import os
+    if not os.path.exists(_lib.LIB_PATH):
+        from paged_mla_decode_04_amd import build
+        build.build()
+    return _lib.load()
+
+
+def units(n):
+    return max(1, -(-int(n) // 64))
+
+
+def seg_cost(q_rows):
+    r = 16 if q_rows <= 16 else 32 if q_rows <= 32 else 64
+    return max(1, (r + 27) // 28)
+
+
+def check_plan(seqlens, q_rows, num_parts, md, ns):
+    b = len(seqlens)
+    md = md.tolist()
+    ns = ns.tolist()
+    assert ns[0] == 0
+    flat = [(s, p) for s in range(b) for p in range(units(seqlens[s]))]
+    covered = []
+    touches = [0] * b
+    for part in md:
+        sb, pb, sl, pe, first = part[:5]
+        assert part[5:] == [0, 0, 0]
+        if sb == b:
+            assert (pb, sl, pe, first) == (0, b, 0, 0)
+            continue
+        assert 0 <= sb <= sl < b
+        assert first == touches[sb]
+        for s in range(sb, sl + 1):
+            lo = pb if s == sb else 0
+            hi = pe if s == sl else units(seqlens[s])
+            assert 0 <= lo < hi <= units(seqlens[s]), (part, s)
+            covered += [(s, p) for p in range(lo, hi)]
+            touches[s] += 1
+    assert covered == flat
+    for s in range(b):
+        assert ns[s + 1] - ns[s] == touches[s]
+    # idle parts only after the busy ones
+    busy = [p[0] < b for p in md]
+    assert busy == sorted(busy, reverse=True)
+    return md
+
+
+def part_cost(part, seqlens, c):
+    sb, pb, sl, pe = part[:4]
+    if sb == len(seqlens):
+        return 0
+    cost = 0
+    for s in range(sb, sl + 1):
+        lo = pb if s == sb else 0
+        hi = pe if s == sl else units(seqlens[s])
+        cost += hi - lo + c
+    return cost
+
+
+CASES = [
+    ([37, 130], 16, 256),
+    ([37, 130], 16, 1),
+    ([37, 130], 16, 2),
+    ([0], 16, 4),
+    ([0, 0, 5], 128, 3),
+    ([64, 65, 1, 128], 128, 5),
+    ([32768] + [1] * 15, 128, 128),
+    (list(range(1, 300, 7)), 256, 64),
+    ([4096] * 128, 128, 128),
+]
+
+
+@pytest.mark.parametrize("seqlens,q_rows,parts", CASES)
+def test_plan_covers_each_unit_once(seqlens, q_rows, parts):
+    md, ns = plan_host(seqlens, q_rows, 1, parts)
+    check_plan(seqlens, q_rows, parts, md, ns)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_plans_are_valid_and_balanced(seed):
+    rng = random.Random(seed)
+    b = rng.randint(1, 200)
+    kind = rng.choice(["uniform", "skew", "tiny", "zeros"])
+    if kind == "uniform":
+        seqlens = [rng.randint(1, 8192) for _ in range(b)]
+    elif kind == "skew":
+        seqlens = [int(2 ** rng.uniform(0, 15)) for _ in range(b)]
+    elif kind == "tiny":
+        seqlens = [rng.randint(0, 70) for _ in range(b)]
+    else:
+        seqlens = [rng.choice([0, 0, 1, 64, 4096]) for _ in range(b)]
+    q_rows = rng.choice([16, 32, 64, 128, 256])
+    parts = rng.choice([1, 2, 7, 64, 128, 256, 1024])
+    md, ns = plan_host(seqlens, q_rows, 1, parts)
+    md = check_plan(seqlens, q_rows, parts, md, ns)
+    c = seg_cost(q_rows)
+    total = sum(units(n) + c for n in seqlens)
+    target = max(c + 1, -(-(total + (parts - 1) * c) // parts))
+    costs = [part_cost(p, seqlens, c) for p in md]
+    # every part but the last stays within its budget
+    busy = [x for x, p in zip(costs, md) if p[0] < b]
+    assert all(x <= target for x in busy[:-1]), (busy, target)
+
+
+def test_grouped_rows_divide_by_kv_heads():
+    a = plan_host([100, 900], 32, 2, 8)
+    b = plan_host([100, 900], 16, 1, 8)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_plan_rejects_bad_arguments():
+    with pytest.raises(ValueError):
+        plan_host([1, 2], 16, 1, 0)
+    with pytest.raises(ValueError):
+        plan_host([1, 2], 4096, 1, 4)
