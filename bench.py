@@ -1,0 +1,194 @@
+"""Benchmark of paged MLA decode on one MI355X.
+
+One step = one pass of the whole hot path over one batch: the split-KV plan
+(mla_get_metadata) and the decode with its lse merge (mla_decode_with_kvcache),
+on synthetic inputs already resident in HBM.  The default workload is the
+wide-head shape of the PAI FlashMLA tutorial's bandwidth plot (segmentfault,
+"云上玩转DeepSeek系列之五", section 二.4): b=128, s_q=1, h_q=128, h_kv=1,
+seqlens ~ N(4096, 1024) clipped to [1, 8192], 64-token pages, identity block
+table, bf16 N(0,1) data.
+
+Throughput uses the tutorial's formulas: bytes = (sum(seqlens) * 576 +
+b * s_q * h_q * (576 + 512)) * 2 and FLOPs = s_q * sum(seqlens) * h_q *
+(576 + 512) * 2, over milliseconds, in decimal GB/s and TFLOPS.
+
+Prints one JSON line.  Runs on one GPU only.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from paged_mla_decode_04_amd import (_lib, default_num_parts, get_mla_metadata,  # noqa: E402
+                                     mla_decode_with_kvcache, workspace_size)
+from paged_mla_decode_04_amd import metrics  # noqa: E402
+from paged_mla_decode_04_amd.workloads import D_V, WORKLOADS, draw  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
+BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, 2.5 PFLOP/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="wide", choices=sorted(WORKLOADS))
+    ap.add_argument("--num-parts", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU-oracle sample budget (whole sequences until this much work)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(inp, budget_s: float):
+    """The fp64 oracle on whole sequences of the same inputs, until budget_s of work."""
+    from oracle import mla_ref
+
+    def raw(t):
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    qb, kb = raw(inp.q), raw(inp.k_storage)
+    bt, sl = inp.block_table.numpy(), inp.cache_seqlens.numpy()
+    w = inp.workload
+    done, elapsed = [], 0.0
+    for b in range(w.batch):
+        t0 = time.perf_counter()
+        mla_ref.mla_decode_ref(qb, kb, bt, sl, w.softmax_scale, w.causal, batch_indices=[b])
+        elapsed += time.perf_counter() - t0
+        done.append(b)
+        if elapsed >= budget_s:
+            break
+    tokens = int(sl[done].sum())
+    nbytes = metrics.decode_bytes(tokens, len(done), w.s_q, w.h_q, w.h_kv)
+    flops = metrics.decode_flops(w.s_q, tokens, w.h_q)
+    threads = None
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 0) for i in threadpoolctl.threadpool_info()
+                      if i.get("user_api") == "blas")
+    except Exception:
+        threads = os.cpu_count()
+    ms = elapsed * 1e3
+    return {"value": round(metrics.gbps(nbytes, ms), 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "tflops": round(metrics.tflops(flops, ms), 6),
+            "seconds": round(elapsed, 3),
+            "sample": f"{len(done)} of {w.batch} sequences ({tokens} cached tokens), fp64 NumPy "
+                      f"oracle, {os.cpu_count()} host cores visible"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU; multi-GPU runs are not "
+                                   "part of this build", "n_gpus": args.gpus}))
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+    _lib.load()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    inp_host = draw(args.workload)
+    inp = inp_host.to(dev)
+    w = inp.workload
+    rows = w.s_q * w.h_q
+    parts = args.num_parts or default_num_parts(rows, w.h_kv)
+    b = w.batch
+    out = torch.empty((b, w.s_q, w.h_q, D_V), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((b, w.s_q, w.h_q), dtype=torch.float32, device=dev)
+    ws = torch.empty((workspace_size(b, w.s_q, w.h_q, w.h_kv, D_V, parts),), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        meta = get_mla_metadata(inp.cache_seqlens, rows, w.h_kv, num_parts=parts)
+        mla_decode_with_kvcache(inp.q, inp.blocked_k, inp.block_table, inp.cache_seqlens, D_V,
+                                w.softmax_scale, w.causal, metadata=meta, out=out, lse=lse,
+                                workspace=ws)
+        return meta
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps; events bracket the decode call of each
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1, e2 in ev:
+        e0.record()
+        meta = get_mla_metadata(inp.cache_seqlens, rows, w.h_kv, num_parts=parts)
+        e1.record()
+        mla_decode_with_kvcache(inp.q, inp.blocked_k, inp.block_table, inp.cache_seqlens, D_V,
+                                w.softmax_scale, w.causal, metadata=meta, out=out, lse=lse,
+                                workspace=ws)
+        e2.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    ms_per_step = wall_ms / args.steps
+    plan_ms = float(np.mean([a.elapsed_time(b_) for a, b_, _ in ev]))
+    decode_ms = np.array([b_.elapsed_time(c) for _, b_, c in ev])
+
+    seqlens = inp_host.cache_seqlens
+    cost = metrics.workload_cost(seqlens.tolist(), b, w.s_q, w.h_q, w.h_kv)
+    gbs = metrics.gbps(cost["bytes"], ms_per_step)
+    tfl = metrics.tflops(cost["flops"], ms_per_step)
+    dec_avg = float(decode_ms.mean())
+    achieved = metrics.gbps(cost["bytes"], dec_avg)
+
+    line = {
+        "metric": "paged MLA decode GB/s + TFLOPS (% roofline), b=128 h_q=128 seqlen~4096",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: {w.description}",
+            "batch": b, "s_q": w.s_q, "h_q": w.h_q, "h_kv": w.h_kv, "d": 576, "dv": 512,
+            "block_size": 64, "entry_pitch": w.pitch, "causal": w.causal,
+            "total_seqlens": cost["total_seqlens"], "num_parts": parts,
+            "parallelism": "single GPU",
+        },
+        "tflops": round(tfl, 2),
+        "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "frac_bf16_peak": round(tfl / BF16_PEAK_TFLOPS, 4),
+        "algorithmic_bytes": cost["bytes"],
+        "algorithmic_flops": cost["flops"],
+        "stage_ms": {"plan": round(plan_ms, 5), "decode_and_merge": round(dec_avg, 5),
+                     "decode_p10": round(float(np.percentile(decode_ms, 10)), 5),
+                     "decode_p90": round(float(np.percentile(decode_ms, 90)), 5)},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "mla_decode_with_kvcache (split-KV decode + lse merge)",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp_host, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
