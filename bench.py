@@ -49,7 +49,21 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU-oracle sample budget (whole sequences until this much work)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (calibrates HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_probe():
+    """A plain copy of known size, to scale profiler byte counters against."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 3}))
 
 
 def cpu_baseline(inp, budget_s: float):
@@ -97,6 +111,9 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
     _lib.load()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     inp_host = draw(args.workload)

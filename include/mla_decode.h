@@ -97,6 +97,7 @@ int mla_default_num_parts(int device, int32_t q_rows, int32_t h_kv, int32_t* num
  *                   first sequence.  An idle part has seq_begin == batch.
  * num_splits_d    : device int32 [batch + 1], written: prefix sums of the number of
  *                   parts that touch each sequence (num_splits[0] = 0).
+ * batch <= 16384 (MLA_ERR_UNSUPPORTED otherwise; mla_plan_host has no limit).
  * The plan depends only on (cache_seqlens, batch, q_rows, h_kv, num_parts), so one plan
  * serves every layer's decode of one step.  Asynchronous; the caller owns all buffers.
  */

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <vector>
 
 #include "../../include/mla_decode.h"
 #include "mla_internal.h"
@@ -29,17 +30,20 @@ int cu_count(int device) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WorkspaceLayout {
-  size_t tile_md, num_splits, part_lse, part_o, total;
+  size_t tile_md, num_splits, part_lse, part_o, flush, total;
 };
 
+// [plan][partial lse][partial O][flush scratch per decode workgroup]
 WorkspaceLayout layout(int64_t batch, int64_t rows, int64_t dv, int64_t num_parts) {
   WorkspaceLayout w;
   const int64_t slots = batch + num_parts;
+  const int64_t workgroups = num_parts * mla::row_blocks((int)rows);
   w.tile_md = 0;
   w.num_splits = align256((size_t)num_parts * mla::kTileMdInts * 4);
   w.part_lse = w.num_splits + align256((size_t)(batch + 1) * 4);
   w.part_o = w.part_lse + align256((size_t)(slots * rows) * 4);
-  w.total = w.part_o + align256((size_t)(slots * rows * dv) * 4);
+  w.flush = w.part_o + align256((size_t)(slots * rows * dv) * 4);
+  w.total = w.flush + align256((size_t)(workgroups * mla::kFlushFloatsPerWorkgroup) * 4);
   return w;
 }
 
@@ -94,7 +98,9 @@ int mla_plan_host(const int32_t* cache_seqlens_h, int32_t batch, int32_t q_rows,
   if ((!cache_seqlens_h && batch > 0) || !tile_md_h || !num_splits_h) return MLA_ERR_NULL_POINTER;
   const int st = check_plan_args(batch, q_rows, h_kv, num_parts);
   if (st != MLA_OK) return st;
-  mla::plan_split_kv(cache_seqlens_h, batch, q_rows / h_kv, num_parts, tile_md_h, num_splits_h);
+  std::vector<int64_t> prefix((size_t)batch + 1);
+  mla::plan_split_kv_host(cache_seqlens_h, batch, q_rows / h_kv, num_parts, tile_md_h, num_splits_h,
+                          prefix.data());
   return MLA_OK;
 }
 
@@ -103,6 +109,7 @@ int mla_get_metadata(const int32_t* cache_seqlens_d, int32_t batch, int32_t q_ro
   if ((!cache_seqlens_d && batch > 0) || !tile_md_d || !num_splits_d) return MLA_ERR_NULL_POINTER;
   const int st = check_plan_args(batch, q_rows, h_kv, num_parts);
   if (st != MLA_OK) return st;
+  if (batch > mla::kMaxPlanBatch) return MLA_ERR_UNSUPPORTED;
   if (mla::launch_plan(cache_seqlens_d, batch, q_rows / h_kv, num_parts, tile_md_d, num_splits_d,
                        (hipStream_t)stream) != hipSuccess)
     return MLA_ERR_HIP;
@@ -171,6 +178,7 @@ int mla_decode_with_kvcache(const mla_decode_params* p, void* stream) {
   const int32_t* tile_md = p->tile_md;
   const int32_t* num_splits = p->num_splits;
   if (!tile_md) {
+    if (p->batch > mla::kMaxPlanBatch) return MLA_ERR_UNSUPPORTED;
     int32_t* md = (int32_t*)(ws + w.tile_md);
     int32_t* ns = (int32_t*)(ws + w.num_splits);
     if (mla::launch_plan(p->cache_seqlens, p->batch, (int)rows, num_parts, md, ns, s) != hipSuccess)
@@ -204,6 +212,7 @@ int mla_decode_with_kvcache(const mla_decode_params* p, void* stream) {
   a.row_blocks = mla::row_blocks((int)rows);
   a.part_lse = (float*)(ws + w.part_lse);
   a.part_o = (float*)(ws + w.part_o);
+  a.flush = (float*)(ws + w.flush);
   a.out = (uint16_t*)p->out;
   a.o_sb = p->out_batch_stride;
   a.o_ss = p->out_seq_stride;

@@ -16,16 +16,20 @@
 //     buffer loads that write LDS directly (no VGPR staging), double
 //     buffered; all 4 waves issue the copies;
 //   * up to 4 compute waves own 16 or 32 query rows each (a workgroup holds
-//     at most 128 rows); the query block stays in registers as MFMA operands
-//     and the 128 x 512 fp32 output accumulator in (accumulation) registers;
+//     at most 128 rows, so every page is read once for 128 heads); the query
+//     block stays in registers as MFMA operands and the fp32 output
+//     accumulator (up to 32 x 512 per wave) in the accumulation registers;
 //   * scores are computed transposed, S^T = K . Q^T, on 16x16x32 bf16 MFMA,
 //     so every lane holds whole query rows: row max / row sum need only two
-//     cross-lane steps and the output rescale is lane-local;
+//     cross-lane steps;
 //   * P . V is computed as O^T = V^T . P^T: P^T comes straight from the score
 //     registers (no data movement) and V^T from LDS with the gfx950
 //     transposing read ds_read_b64_tr_b16 (4 consecutive tokens per lane);
-//   * online softmax in the log2 domain; the running max is only moved when
-//     it grows by more than 2^8, so the output is rescaled rarely;
+//   * online softmax in the log2 domain.  The reference max only moves when a
+//     row's score exceeds it by more than 2^16; then (rarely) the wave flushes
+//     its unscaled accumulator into a carry in global scratch instead of
+//     rescaling it in registers, so no vector ALU op touches the accumulator
+//     inside the page loop;
 //   * a part that covers only a piece of a sequence writes an fp32 partial
 //     (O / l, lse); the merge kernel combines them by lse (Flash-Decoding, as
 //     the Hacker News discussion of the FlashMLA release describes it).
@@ -48,11 +52,12 @@ namespace mla {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) int32_t lds_i32;
 
 constexpr int kD = 576;
 constexpr int kDv = 512;
@@ -62,7 +67,7 @@ constexpr int kKSteps = kD / 32;          // 18 MFMA k-steps of 32 for the score
 constexpr int kColTiles = kDv / 16;       // 32 output column tiles of 16
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kRescaleSlack = 8.0f;     // log2 units: p = 2^(x - m) stays <= 256
+constexpr float kRescaleSlack = 16.0f;    // log2 units: p = 2^(x - m) stays <= 65536
 constexpr int32_t kBufferFlags = 0x00020000;
 constexpr uint32_t kOutOfRange = 0x7FFFF000u;
 
@@ -79,47 +84,23 @@ __device__ __forceinline__ float wave_sum16(float v) {
   return v;
 }
 
-// Workgroup barrier for LDS hand-offs.  The page copies are waited for
-// explicitly (vmcnt) before it; unlike __syncthreads it does not also wait for
-// the next page's copies still in flight.
-// Register-class hints (emit no instructions): the 128 x 512 fp32 output
-// accumulator lives in the accumulation registers, the query fragments in
-// ordinary VGPRs, so that together they fit one wave's 512 registers.
+// Register-class hints (emit no instructions): the output accumulator lives
+// in the accumulation registers, scores in ordinary VGPRs, so that the query
+// fragments, scores and accumulator fit one wave's 512 registers.
 __device__ __forceinline__ void pin_acc(f32x4& x) { asm volatile("" : "+a"(x)); }
-__device__ __forceinline__ void pin_vgpr(bf16x8& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin_vgpr(f32x4& x) { asm volatile("" : "+v"(x)); }
 
-// x *= alpha for an accumulator element kept in an accumulation register.  One
-// opaque read-multiply-write, so the copy through a VGPR happens here and only
-// here (the compiler would otherwise keep a VGPR copy of every accumulator
-// alive across the page loop for this rarely taken path).  Callers run it far
-// from the MFMAs that write or read these accumulators.
-__device__ __forceinline__ void scale_acc1(float& x, float alpha) {
-  float t;
-  asm volatile(
-      "v_accvgpr_read_b32 %1, %0\n\t"
-      "v_mul_f32_e32 %1, %2, %1\n\t"
-      "s_nop 1\n\t"
-      "v_accvgpr_write_b32 %0, %1"
-      : "+a"(x), "=&v"(t)
-      : "v"(alpha));
-}
-__device__ __forceinline__ void scale_acc(f32x4& o, float alpha) {
-  float x0 = o[0], x1 = o[1], x2 = o[2], x3 = o[3];
-  scale_acc1(x0, alpha);
-  scale_acc1(x1, alpha);
-  scale_acc1(x2, alpha);
-  scale_acc1(x3, alpha);
-  o = f32x4{x0, x1, x2, x3};
-  pin_acc(o);
-}
-
-// Opaque copy of a pointer: keeps base + constant address arithmetic from being
-// re-associated (and hoisted) so the constant lands in the instruction offset.
+// Opaque copy of an LDS pointer: keeps base + constant address arithmetic from
+// being re-associated (and hoisted) so the constant lands in the instruction
+// offset field.
 __device__ __forceinline__ lds_u8* launder(lds_u8* p) {
   asm volatile("" : "+v"(p));
   return p;
 }
 
+// Workgroup barrier for LDS hand-offs.  The page copies are waited for
+// explicitly (vmcnt) before it; unlike __syncthreads it does not also wait for
+// the next page's copies still in flight.
 __device__ __forceinline__ void block_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Nine 16-byte LDS-direct loads: chunk octets 0..8 of one token octet.  The
@@ -154,144 +135,289 @@ __device__ __forceinline__ void copy_page(const DecodeArgs& a, int phys, bool va
   }
 }
 
-constexpr int kLatentSteps = kDv / 32;  // k-steps whose Q fragments live in registers
-constexpr int kRopeSteps = kKSteps - kLatentSteps;
-constexpr int kQRopeOffset = 2 * kPageBytes;            // LDS bytes: after the two page tiles
-constexpr int kQRopeWaveBytes = 2 * kRopeSteps * 64 * 16;  // RT <= 2 row tiles per wave
-constexpr int kSmemBytes = kQRopeOffset + 4 * kQRopeWaveBytes;  // 163840
-
-template <int RT>  // row tiles of 16 per compute wave
+// Per-wave state.  A compute wave owns 16 query rows for the scores and the
+// softmax (lane row l % 16), and one column block of the output accumulator
+// for all the workgroup's rows: NWC row tiles x (32 / NWC) column tiles of
+// 16 x 16, always 128 accumulation registers.
+template <int NWC>
 struct WaveState {
-  bf16x8 qf[RT][kLatentSteps];  // Q^T operand fragments of the 512 latent columns
-  f32x4 o[kColTiles][RT];       // O^T accumulators: lane row, columns 16 ct + 4 g + j
-  float m[RT];                  // running max (log2 units of scaled scores)
-  float l[RT];                  // running sum of the bf16-rounded probabilities P . V used
-  float le[RT];                 // running sum of the unrounded probabilities (for lse)
+  static constexpr int kCT = kColTiles / NWC;  // column tiles of this wave's block
+  bf16x8 qf[kKSteps];       // Q^T operand fragments of the wave's 16 rows
+  f32x4 o[kCT][NWC];        // O^T accumulators: [column tile][row tile]
+  float m, l, le;           // own row: reference max (log2 units), sums of rounded /
+                            // unrounded probabilities
+  float cm, cl, cle;        // own row: the carry's reference and sums
+  bool carry;               // workgroup-uniform: the carry holds a flushed accumulator
 };
 
-// One page in two halves of 32 tokens.  Per half: S^T = K . Q^T (16x16x32 MFMA,
-// the 64 rope columns' Q fragments read back from LDS), mask, online softmax,
-// O^T += V^T . P^T.  `vis` is this lane's visible-token count per row tile,
-// relative to the page start (>= 64 when nothing is masked).
-template <int RT>
-__device__ __forceinline__ void compute_page(const DecodeArgs& a, WaveState<RT>& st, lds_u8* qrope,
-                                             int lane, const int* vis, lds_u8* kb0, lds_u8* kb1,
-                                             lds_u8* const* vb) {
+// Fold the accumulator into the carry: carry = carry * fc[row] + O (O unscaled),
+// then O = 0.  The accumulator is only stored (from the accumulation registers),
+// never operated on by vector ALU instructions, so the page loop keeps it in
+// AGPRs; the dump is read back as fresh values.
+template <int NWC>
+__device__ __forceinline__ void fold_into_carry(WaveState<NWC>& st, float* carry, float* dump, int lane,
+                                                const lds_f32* fc) {
+  constexpr int kCT = WaveState<NWC>::kCT;
+  constexpr int kStride = kCT * 16;
   const int g = lane >> 4;
 #pragma unroll
+  for (int rt = 0; rt < NWC; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < kCT; ++ct)
+      *(f32x4*)(dump + (16 * rt + (lane & 15)) * kStride + 16 * ct + 4 * g) = st.o[ct][rt];
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int rt = 0; rt < NWC; ++rt) {
+    const float f = st.carry ? fc[16 * rt + (lane & 15)] : 0.f;
+#pragma unroll 2
+    for (int ct = 0; ct < kCT; ++ct) {
+      float* cp = carry + (16 * rt + (lane & 15)) * kStride + 16 * ct + 4 * g;
+      float* dp = dump + (16 * rt + (lane & 15)) * kStride + 16 * ct + 4 * g;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float d = __hip_atomic_load(dp + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float c = st.carry ? __hip_atomic_load(cp + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.f;
+        __hip_atomic_store(cp + j, c * f + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < kCT; ++ct) {
+      st.o[ct][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      pin_acc(st.o[ct][rt]);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// LDS fragments are fetched a fixed number of steps ahead into explicit
+// register buffers, and consecutive MFMAs accumulate into different tiles, so
+// neither LDS latency nor the MFMA dependency chain is exposed; scheduling
+// barriers pin that order.
+constexpr int kAheadK = 2;  // score k-steps (4 fragments each)
+constexpr int kAheadV = 3;  // output column tiles (one transposed fragment each)
+
+// LDS regions next to the two page tiles.
+constexpr int kPFragOffset = 2 * kPageBytes;                   // P^T fragments [row tile][half][lane]
+constexpr int kStatsOffset = kPFragOffset + 4 * 2 * 64 * 16;   // fc / wo / wc [64 rows], flags[4]
+constexpr int kSmemBytes = kStatsOffset + 3 * 64 * 4 + 16;
+
+struct Lds {
+  lds_u8* base;
+  __device__ lds_bf16x8* pfrag(int rt, int half) const {
+    return (lds_bf16x8*)(base + kPFragOffset + (rt * 2 + half) * 1024);
+  }
+  __device__ lds_f32* fc() const { return (lds_f32*)(base + kStatsOffset); }
+  __device__ lds_f32* wo() const { return (lds_f32*)(base + kStatsOffset + 256); }
+  __device__ lds_f32* wc() const { return (lds_f32*)(base + kStatsOffset + 512); }
+  __device__ lds_i32* flags() const { return (lds_i32*)(base + kStatsOffset + 768); }
+};
+
+// One 64-token page for compute wave `wave`.  Scores and softmax for the
+// wave's own 16 rows; P^T fragments go through LDS to every compute wave;
+// each wave then adds V^T . P^T into its column block for all the rows.
+// `vis` is the own row's visible-token count relative to the page start.
+// Contains one workgroup barrier that the non-computing waves match with
+// page_barrier_for_idle().
+template <int NWC>
+__device__ __forceinline__ void compute_page(const DecodeArgs& a, WaveState<NWC>& st, const Lds& L, int wave,
+                                             int lane, int vis, lds_u8* kb0, lds_u8* kb1, lds_u8* const* vb,
+                                             float* carry, float* dump) {
+  constexpr int kCT = WaveState<NWC>::kCT;
+  const int g = lane >> 4;
+  // ---- scores of the own 16 rows: 4 token tiles, 18 k-steps
+  f32x4 s[4];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 kf[kKSteps][4];
+  auto load_k = [&](int ks) {
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+      kf[ks][tt] = *(const lds_bf16x8*)(((ks & 1) ? kb1 : kb0) + 18432u * tt + 1024u * (ks >> 1));
+  };
+#pragma unroll
+  for (int ks = 0; ks < kAheadK; ++ks) load_k(ks);
+#pragma unroll
+  for (int ks = 0; ks < kKSteps; ++ks) {
+    if (ks + kAheadK < kKSteps) load_k(ks + kAheadK);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+      s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks][tt], st.qf[ks], s[tt], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) pin_vgpr(s[tt]);
+
+  // ---- mask (token 16 tt + 4 g + j visible iff < vis), scale, row max
+  const int lim = vis - 4 * g;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float x = (16 * tt + j < lim) ? s[tt][j] * a.scale_log2 : -INFINITY;
+      s[tt][j] = x;
+      mx = fmaxf(mx, x);
+    }
+  mx = wave_max16(mx);
+  // The reference max is set on the row's first visible key and moved only when
+  // a finite reference is exceeded by more than the slack; then the whole
+  // workgroup folds its accumulator into the carry (below).
+  const bool over = (st.m != -INFINITY) && (mx > st.m + kRescaleSlack);
+  const float fc = st.carry ? __builtin_amdgcn_exp2f(st.cm - st.m) : 0.f;  // carry factor at the old reference
+  const float m_new = over ? fmaxf(st.m, mx) : (st.m == -INFINITY ? mx : st.m);
+  // probabilities (bf16 P^T fragments per 32-token half) and their sums
+  const float mu = (m_new == -INFINITY) ? 0.f : m_new;
+  bf16x8 pf[2];
+  float sum = 0.f, sum_exact = 0.f;
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float e = __builtin_amdgcn_exp2f(s[tt][j] - mu);
+      const __bf16 p = (__bf16)e;
+      sum += (float)p;
+      sum_exact += e;
+      pf[tt >> 1][4 * (tt & 1) + j] = p;
+    }
+  sum = wave_sum16(sum);
+  sum_exact = wave_sum16(sum_exact);
+  L.pfrag(wave, 0)[lane] = pf[0];
+  L.pfrag(wave, 1)[lane] = pf[1];
+  if (g == 0) L.fc()[16 * wave + lane] = fc;
+  const bool wave_over = __builtin_amdgcn_ballot_w64(over) != 0;
+  if (lane == 0) L.flags()[wave] = wave_over ? 1 : 0;
+  block_sync();
+
+  bool flush = false;
+#pragma unroll
+  for (int w = 0; w < NWC; ++w) flush |= L.flags()[w] != 0;
+  if (flush) {  // rare: fold everything accumulated so far into the carry
+    fold_into_carry<NWC>(st, carry, dump, lane, L.fc());
+    st.cl = st.cl * fc + st.l;
+    st.cle = st.cle * fc + st.le;
+    st.cm = st.m;
+    st.l = sum;
+    st.le = sum_exact;
+    st.carry = true;
+  } else {
+    st.l += sum;
+    st.le += sum_exact;
+  }
+  st.m = m_new;
+
+  // ---- O^T[column block] += V^T . P^T over both halves, all row tiles
+#pragma unroll
   for (int half = 0; half < 2; ++half) {
-    f32x4 s[2][RT];
+    bf16x8 pr[NWC];
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) s[t2][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bf16x8 qr[RT][kRopeSteps];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int k = 0; k < kRopeSteps; ++k)
-        qr[rt][k] = *(const lds_bf16x8*)(qrope + (rt * kRopeSteps + k) * 1024 + lane * 16);
-#pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      const int tt = 2 * half + t2;
-#pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) {
-        const bf16x8 kf = *(const lds_bf16x8*)(((ks & 1) ? kb1 : kb0) + 18432u * tt + 1024u * (ks >> 1));
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          const bf16x8 qv = ks < kLatentSteps ? st.qf[rt][ks < kLatentSteps ? ks : 0]
-                                              : qr[rt][ks < kLatentSteps ? 0 : ks - kLatentSteps];
-          s[t2][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qv, s[t2][rt], 0, 0, 0);
-        }
-      }
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4 + RT * kRopeSteps, 0);
-#pragma unroll
-    for (int i = 0; i < 2 * kKSteps; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, RT, 0);
-      if (i < 2 * kKSteps - 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-
-    // mask (token 32 half + 16 t2 + 4 g + j visible iff < vis), scale, row max
-    float mx[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int lim = vis[rt] - 32 * half - 4 * g;
-      float v = -INFINITY;
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float x = (16 * t2 + j < lim) ? s[t2][rt][j] * a.scale_log2 : -INFINITY;
-          s[t2][rt][j] = x;
-          v = fmaxf(v, x);
-        }
-      mx[rt] = wave_max16(v);
-    }
-    bool grow = false;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) grow |= (mx[rt] > st.m[rt] + kRescaleSlack);
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const float mnew = fmaxf(st.m[rt], mx[rt]);
-        const float alpha = __builtin_amdgcn_exp2f(st.m[rt] - (mnew == -INFINITY ? 0.f : mnew));
-        st.m[rt] = mnew;
-        st.l[rt] *= alpha;
-        st.le[rt] *= alpha;
-#pragma unroll
-        for (int ct = 0; ct < kColTiles; ++ct) scale_acc(st.o[ct][rt], alpha);
-      }
-    }
-    bf16x8 pf[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const float mu = (st.m[rt] == -INFINITY) ? 0.f : st.m[rt];
-      float sum = 0.f, sum_exact = 0.f;
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float e = __builtin_amdgcn_exp2f(s[t2][rt][j] - mu);
-          const __bf16 p = (__bf16)e;
-          sum += (float)p;
-          sum_exact += e;
-          pf[rt][4 * t2 + j] = p;
-        }
-      st.l[rt] += wave_sum16(sum);
-      st.le[rt] += wave_sum16(sum_exact);
-    }
-
-    // O^T += V^T . P^T over this half's 32 tokens
-#pragma unroll
-    for (int ct = 0; ct < kColTiles; ++ct) {
+    for (int rt = 0; rt < NWC; ++rt) pr[rt] = L.pfrag(rt, half)[lane];
+    bf16x8 vf[kCT];
+    auto load_v = [&](int ct) {
       lds_u8* vp = vb[ct & 3] + 9216u * (4 * half) + 1024u * (ct >> 2);
       const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)vp);
       const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 2 * 9216u));
-      const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      vf[ct] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        st.o[ct][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rt], st.o[ct][rt], 0, 0, 0);
+    for (int ct = 0; ct < kAheadV && ct < kCT; ++ct) load_v(ct);
+#pragma unroll
+    for (int ct = 0; ct < kCT; ++ct) {
+      if (ct + kAheadV < kCT) load_v(ct + kAheadV);
+#pragma unroll
+      for (int rt = 0; rt < NWC; ++rt) {
+        st.o[ct][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[ct], pr[rt], st.o[ct][rt], 0, 0, 0);
         pin_acc(st.o[ct][rt]);
       }
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 1);
-#pragma unroll
-    for (int i = 0; i < kColTiles; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, RT, 1);
-      if (i < kColTiles - 3) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
 
-// NWC compute waves of RT*16 rows each; all 4 waves copy pages.
-template <int NWC, int RT>
+// Segment epilogue, in two steps around a workgroup barrier (which the idle
+// waves match): each row's owner turns its statistics (with the carry, if the
+// workgroup flushed) into output weights and the lse; then every compute wave
+// writes its column block of every row, as bf16 output or fp32 partial.
+template <int NWC>
+__device__ __forceinline__ void publish_row_weights(const DecodeArgs& a, const WaveState<NWC>& st, const Lds& L,
+                                                    int wave, int lane, int row, int b, bool bad, bool final_out,
+                                                    int slot) {
+  float M = st.m, fo = 1.f, fc = 0.f;
+  if (st.carry) {
+    M = fmaxf(st.cm, st.m);
+    fo = st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.m - M);
+    fc = st.cm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.cm - M);
+  }
+  const float Lr = st.l * fo + st.cl * fc;
+  const float LE = st.le * fo + st.cle * fc;
+  float inv = Lr > 0.f ? 1.f / Lr : 0.f;
+  float lse = LE > 0.f ? (M + __builtin_amdgcn_logf(LE)) * kLn2 : -INFINITY;
+  if (bad) {
+    inv = __builtin_nanf("");
+    lse = __builtin_nanf("");
+  }
+  if ((lane >> 4) == 0) {
+    L.wo()[16 * wave + lane] = fo * inv;
+    L.wc()[16 * wave + lane] = fc * inv;
+    if (row < a.rows) {
+      const int qi = row / a.h_q, h = row - qi * a.h_q;
+      if (final_out)
+        a.lse[(int64_t)b * a.l_sb + (int64_t)qi * a.l_ss + (int64_t)h * a.l_sh] = lse;
+      else
+        a.part_lse[(int64_t)slot * a.rows + row] = lse;
+    }
+  }
+}
+
+template <int NWC>
+__device__ __forceinline__ void write_block(const DecodeArgs& a, const WaveState<NWC>& st, const Lds& L,
+                                            const float* carry, int wave, int lane, int blk_row0, int b,
+                                            bool final_out, int slot) {
+  constexpr int kCT = WaveState<NWC>::kCT;
+  constexpr int kStride = kCT * 16;
+  const int g = lane >> 4;
+#pragma unroll
+  for (int rt = 0; rt < NWC; ++rt) {
+    const int r = blk_row0 + 16 * rt + (lane & 15);
+    const float wo = L.wo()[16 * rt + (lane & 15)];
+    const float wc = L.wc()[16 * rt + (lane & 15)];
+    const bool ok = r < a.rows;
+    const int rr = ok ? r : 0;
+    const int qi = rr / a.h_q, h = rr - qi * a.h_q;
+    const int col0 = wave * kCT * 16 + 4 * g;
+    const float* cp = carry + (16 * rt + (lane & 15)) * kStride + 4 * g;
+    if (final_out) {
+      uint16_t* op = a.out + (int64_t)b * a.o_sb + (int64_t)qi * a.o_ss + (int64_t)h * a.o_sh + col0;
+#pragma unroll
+      for (int ct = 0; ct < kCT; ++ct) {
+        f32x4 v = st.o[ct][rt] * wo;
+        if (st.carry) v += *(const f32x4*)(cp + 16 * ct) * wc;
+        const bf16x4 w = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+        if (ok) *(bf16x4*)(op + 16 * ct) = w;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      float* pp = a.part_o + ((int64_t)slot * a.rows + rr) * kDv + col0;
+#pragma unroll
+      for (int ct = 0; ct < kCT; ++ct) {
+        f32x4 v = st.o[ct][rt] * wo;
+        if (st.carry) v += *(const f32x4*)(cp + 16 * ct) * wc;
+        if (ok) *(f32x4*)(pp + 16 * ct) = v;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+}
+
+// NWC compute waves (16 rows each for the scores, one column block each for
+// the output); all 4 waves copy pages.
+template <int NWC>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmemBytes];
   const int wave = uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
-  constexpr int kBlockRows = NWC * RT * 16;
+  constexpr int kBlockRows = NWC * 16;
+  constexpr int kCT = WaveState<NWC>::kCT;
 
   // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a contiguous run
   // of parts so neighbouring pieces of one sequence share that XCD's L2.
@@ -318,11 +444,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   const int va = 4 * (g & 1) + (vs >> 2);
   const int vR = (g >> 1) & 1;
   const uint32_t vy = (uint32_t)(((vs & 3) >> 1) ^ va ^ vR);
-  const uint32_t vb_lane = 9216u * (g >> 1) + 128u * va + 8u * (vs & 1);
+  // this wave's column block starts at column tile wave * kCT (a multiple of 4)
+  const uint32_t vb_lane = 9216u * (g >> 1) + 128u * va + 8u * (vs & 1) + 1024u * (wave * kCT / 4);
 
   const bool computes = wave < NWC;
-  const int row0 = mblock * kBlockRows + wave * RT * 16;  // first row of this wave
-  WaveState<RT> st;
+  const int blk_row0 = mblock * kBlockRows;
+  const int own_row = blk_row0 + 16 * wave + (lane & 15);
+  // this wave's flush scratch: carry, then dump, 16 * NWC rows x its columns
+  float* carry = a.flush + ((int64_t)hw * 4 + wave) * (2 * 16 * kDv);
+  float* dump = carry + 16 * kDv;
+  const Lds L{(lds_u8*)smem};
+  WaveState<NWC> st;
 
   for (int b = seq_begin; b <= seq_last; ++b) {
     int n = uniform(a.seqlens[b]);
@@ -337,41 +469,34 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     const int slot = uniform(a.num_splits[b]) + split;
     const int32_t* table = a.block_table + (int64_t)b * a.bt_stride;
 
-    lds_u8* qrope = (lds_u8*)smem + kQRopeOffset + wave * kQRopeWaveBytes;
     if (computes) {
+      const bool ok = own_row < a.rows;
+      const int rr = ok ? own_row : 0;
+      const uint16_t* qp = a.q + (int64_t)b * a.q_sb + (int64_t)(rr / a.h_q) * a.q_ss +
+                           (int64_t)(rr % a.h_q) * a.q_sh + 8 * g;
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const int r = row0 + 16 * rt + (lane & 15);
-        const bool ok = r < a.rows;
-        const int rr = ok ? r : 0;
-        const uint16_t* qp = a.q + (int64_t)b * a.q_sb + (int64_t)(rr / a.h_q) * a.q_ss +
-                             (int64_t)(rr % a.h_q) * a.q_sh + 8 * g;
+      for (int ks = 0; ks < kKSteps; ++ks) {
+        bf16x8 v = *(const bf16x8*)(qp + 32 * ks);
+        if (!ok) v = bf16x8{};
+        st.qf[ks] = v;
+      }
+      st.m = -INFINITY;
+      st.l = 0.f;
+      st.le = 0.f;
+      st.cm = -INFINITY;
+      st.cl = 0.f;
+      st.cle = 0.f;
+      st.carry = false;
 #pragma unroll
-        for (int ks = 0; ks < kKSteps; ++ks) {
-          bf16x8 v = *(const bf16x8*)(qp + 32 * ks);
-          if (!ok) v = bf16x8{};
-          if (ks < kLatentSteps)
-            st.qf[rt][ks < kLatentSteps ? ks : 0] = v;
-          else  // rope fragments wait in this wave's LDS slice, in lane order
-            *(lds_bf16x8*)(qrope + (rt * kRopeSteps + ks - kLatentSteps) * 1024 + lane * 16) = v;
-        }
-        st.m[rt] = -INFINITY;
-        st.l[rt] = 0.f;
-        st.le[rt] = 0.f;
+      for (int rt = 0; rt < NWC; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < kColTiles; ++ct) {
+        for (int ct = 0; ct < kCT; ++ct) {
           st.o[ct][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
           pin_acc(st.o[ct][rt]);
         }
-      }
     }
-    // visible keys of this lane's rows: n, or n - (s_q - 1 - i) for query token i
-    int vis_row[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int r = row0 + 16 * rt + (lane & 15);
-      vis_row[rt] = a.causal ? n - (a.s_q - 1 - r / a.h_q) : n;
-    }
+    // visible keys of the own row: n, or n - (s_q - 1 - i) for query token i
+    const int vis_row = a.causal ? n - (a.s_q - 1 - own_row / a.h_q) : n;
     bool bad = false;
     // page p has tokens [64 p, min(64 p + 64, n)); pages with none are skipped
     auto page_tokens = [&](int p) { int t = n - 64 * p; return t > 64 ? 64 : t; };
@@ -401,59 +526,28 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
       else
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
       block_sync();
-      if (computes && tok > 0 && pending) {
-        int vis[RT];
+      if (tok > 0 && pending) {
+        if (computes) {
+          // per-page base addresses; every access adds a constant that fits the
+          // LDS instruction's 16-bit offset field
+          lds_u8* tile = (lds_u8*)smem + buf * kPageBytes;
+          lds_u8* vb[4];
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) vis[rt] = vis_row[rt] - 64 * p;
-        // per-page base addresses; every access adds a constant that fits the
-        // LDS instruction's 16-bit offset field
-        lds_u8* tile = (lds_u8*)smem + buf * kPageBytes;
-        lds_u8* vb[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) vb[u] = launder(tile + vb_lane + 16u * (vy ^ (2u * u)));
-        compute_page<RT>(a, st, qrope, lane, vis, launder(tile + kb_lane + 16u * kx),
-                         launder(tile + kb_lane + 16u * (kx ^ 4u)), vb);
+          for (int u = 0; u < 4; ++u) vb[u] = launder(tile + vb_lane + 16u * (vy ^ (2u * u)));
+          compute_page<NWC>(a, st, L, wave, lane, vis_row - 64 * p, launder(tile + kb_lane + 16u * kx),
+                            launder(tile + kb_lane + 16u * (kx ^ 4u)), vb, carry, dump);
+        } else {
+          block_sync();  // matches the P hand-off barrier inside compute_page
+        }
       }
       block_sync();
       pending = next;
       buf ^= 1;
     }
 
-    // ---- epilogue: final output, or an fp32 partial for the merge
-    if (computes) {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const int r = row0 + 16 * rt + (lane & 15);
-        if (r >= a.rows) continue;
-        const float l = st.l[rt];
-        float inv = l > 0.f ? 1.f / l : 0.f;
-        float lse = l > 0.f ? (st.m[rt] + __builtin_amdgcn_logf(st.le[rt])) * kLn2 : -INFINITY;
-        if (bad) {
-          inv = __builtin_nanf("");
-          lse = __builtin_nanf("");
-        }
-        const int qi = r / a.h_q, h = r - qi * a.h_q;
-        if (nsplit == 1) {
-          uint16_t* op = a.out + (int64_t)b * a.o_sb + (int64_t)qi * a.o_ss + (int64_t)h * a.o_sh + 4 * g;
-#pragma unroll
-          for (int ct = 0; ct < kColTiles; ++ct) {
-            const f32x4 v = st.o[ct][rt] * inv;
-            bf16x4 w = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-            *(bf16x4*)(op + 16 * ct) = w;
-            __builtin_amdgcn_sched_barrier(0);
-          }
-          if (g == 0) a.lse[(int64_t)b * a.l_sb + (int64_t)qi * a.l_ss + (int64_t)h * a.l_sh] = lse;
-        } else {
-          float* pp = a.part_o + ((int64_t)slot * a.rows + r) * kDv + 4 * g;
-#pragma unroll
-          for (int ct = 0; ct < kColTiles; ++ct) {
-            *(f32x4*)(pp + 16 * ct) = st.o[ct][rt] * inv;
-            __builtin_amdgcn_sched_barrier(0);
-          }
-          if (g == 0) a.part_lse[(int64_t)slot * a.rows + r] = lse;
-        }
-      }
-    }
+    if (computes) publish_row_weights<NWC>(a, st, L, wave, lane, own_row, b, bad, nsplit == 1, slot);
+    block_sync();
+    if (computes) write_block<NWC>(a, st, L, carry, wave, lane, blk_row0, b, nsplit == 1, slot);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     block_sync();
   }
@@ -511,14 +605,65 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   if (lane == 0) a.lse[(int64_t)b * a.l_sb + (int64_t)qi * a.l_ss + (int64_t)h * a.l_sh] = L;
 }
 
-__global__ void plan_kernel(const int32_t* seqlens, int batch, int rows, int num_parts, int32_t* tile_md,
-                            int32_t* num_splits) {
-  if (threadIdx.x == 0 && blockIdx.x == 0) plan_split_kv(seqlens, batch, rows, num_parts, tile_md, num_splits);
+// Block-wide inclusive scan step over one 1024-entry chunk (16 waves).
+template <typename T>
+__device__ __forceinline__ T block_inclusive_scan(T v, T* wave_tot, T* carry) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const T t = __shfl_up(v, d);
+    if (lane >= d) v += t;
+  }
+  if (lane == 63) wave_tot[wv] = v;
+  __syncthreads();
+  T add = *carry;
+  for (int w = 0; w < wv; ++w) add += wave_tot[w];
+  __syncthreads();
+  if (tid == 1023) *carry = add + v;
+  return add + v;
+}
+
+// The plan of mla_plan.h on one workgroup: prefix sums of the per-sequence
+// costs in LDS, one binary search per part, a scan of the per-sequence touch
+// counts.  Identical to the host mirror by construction (same integer math).
+__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* seqlens, int batch, int rows, int num_parts,
+                                                    int32_t* tile_md, int32_t* num_splits) {
+  __shared__ int64_t prefix[kMaxPlanBatch + 1];
+  __shared__ int64_t wave_tot64[16];
+  __shared__ int64_t carry64;
+  __shared__ int32_t wave_tot32[16];
+  __shared__ int32_t carry32;
+  const int tid = threadIdx.x;
+  const int c = segment_cost(rows_per_block(rows));
+  if (tid == 0) {
+    prefix[0] = 0;
+    carry64 = 0;
+    carry32 = 0;
+    num_splits[0] = 0;
+  }
+  __syncthreads();
+  for (int base = 0; base < batch; base += 1024) {
+    const int i = base + tid;
+    const int64_t v = i < batch ? (int64_t)(c + seq_units(seqlens[i])) : 0;
+    const int64_t incl = block_inclusive_scan<int64_t>(v, wave_tot64, &carry64);
+    if (i < batch) prefix[i + 1] = incl;
+    __syncthreads();
+  }
+  const int64_t T = plan_stride(prefix[batch], num_parts, c);
+  for (int p = tid; p < num_parts; p += 1024)
+    plan_part(prefix, seqlens, batch, c, T, p, tile_md + (int64_t)p * kTileMdInts);
+  for (int base = 0; base < batch; base += 1024) {
+    const int i = base + tid;
+    const int32_t v = i < batch ? plan_touches(prefix, i, c, T) : 0;
+    const int32_t incl = block_inclusive_scan<int32_t>(v, wave_tot32, &carry32);
+    if (i < batch) num_splits[i + 1] = incl;
+    __syncthreads();
+  }
 }
 
 hipError_t launch_plan(const int32_t* seqlens, int batch, int rows, int num_parts, int32_t* tile_md,
                        int32_t* num_splits, hipStream_t stream) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(64), 0, stream, seqlens, batch, rows, num_parts, tile_md,
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, seqlens, batch, rows, num_parts, tile_md,
                      num_splits);
   return hipGetLastError();
 }
@@ -527,11 +672,11 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)(a.num_parts * a.row_blocks));
   const int rpb = rows_per_block(a.rows);
   if (rpb == 16)
-    hipLaunchKernelGGL((decode_kernel<1, 1>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<1>), grid, dim3(kThreads), 0, stream, a);
   else if (rpb == 32)
-    hipLaunchKernelGGL((decode_kernel<2, 1>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<2>), grid, dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_kernel<4, 1>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<4>), grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

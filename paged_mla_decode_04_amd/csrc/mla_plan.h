@@ -10,19 +10,23 @@
 //   * work unit = one 64-token page of one sequence; a sequence with no
 //     tokens still owns one (empty) unit so that some part writes its
 //     result (out = 0, lse = -inf);
-//   * the flattened (sequence, page) order is cut into num_parts contiguous
-//     ranges of near-equal cost, cost = pages + segment_cost per
-//     (part, sequence) pair: a piece of a sequence pays for loading its
-//     queries and for writing (and later merging) its result;
+//   * every sequence also carries a fixed cost c: a piece of a sequence
+//     loads its queries and writes (and later merges) its result;
+//   * lay the sequences end to end on a cost axis: sequence b occupies
+//     positions [S_b, S_{b+1}) with S_{b+1} = S_b + c + units_b (its c
+//     overhead positions first, then one position per page); W = S_batch;
+//   * part p owns positions [p T, (p+1) T) with T = max(c + 1, ceil(W / P)),
+//     so parts are contiguous, in order, and never empty;
 //   * part p is [seq_begin, page_begin, seq_last, page_end, split_first,
-//     0, 0, 0]: pages from (seq_begin, page_begin) to (seq_last,
-//     page_end - 1); split_first is how many earlier parts touched
-//     seq_begin; an idle part has seq_begin = batch;
+//     0, 0, 0]: pages (seq_begin, page_begin) .. (seq_last, page_end - 1);
+//     split_first is the number of earlier parts that touched seq_begin;
+//     an idle part (p T >= W) has seq_begin = batch;
 //   * num_splits[b + 1] - num_splits[b] is the number of parts that touch
 //     sequence b (num_splits[0] = 0); a sequence touched once needs no merge.
 //
-// The same function runs in the host mirror and in the one-thread plan
-// kernel, so both produce identical plans.
+// Everything is closed-form integer arithmetic on prefix sums, so the host
+// mirror below and the one-workgroup device kernel (a block scan plus one
+// binary search per part) produce identical plans.
 #pragma once
 #include <stdint.h>
 
@@ -37,9 +41,10 @@ namespace mla {
 constexpr int kPageTokens = 64;
 constexpr int kTileMdInts = 8;
 constexpr int kRowsPerWorkgroup = 64;
+constexpr int kMaxPlanBatch = 16384;  // device plan keeps the prefix sums in LDS
 
-// Rows one workgroup handles when the kv head has `rows` query rows (16 per
-// compute wave, up to 4 compute waves).
+// Rows one workgroup handles when the kv head has `rows` query rows: up to 4
+// compute waves of 16 rows.
 MLA_HD inline int rows_per_block(int rows) {
   if (rows <= 16) return 16;
   if (rows <= 32) return 32;
@@ -66,68 +71,77 @@ MLA_HD inline int seq_units(int32_t n) {
   return (int)u;
 }
 
-MLA_HD inline void plan_split_kv(const int32_t* seqlens, int batch, int q_rows_per_kv_head,
-                                 int num_parts, int32_t* tile_md, int32_t* num_splits) {
-  const int c = segment_cost(rows_per_block(q_rows_per_kv_head));
-  int64_t total = 0;
-  for (int b = 0; b < batch; ++b) total += seq_units(seqlens[b]) + c;
-  // Each cut inside a sequence costs one more segment; at most num_parts - 1 cuts.
-  int64_t target = (total + (int64_t)(num_parts - 1) * c + num_parts - 1) / num_parts;
-  if (target < c + 1) target = c + 1;
+MLA_HD inline int64_t plan_stride(int64_t total, int num_parts, int c) {
+  int64_t t = (total + num_parts - 1) / num_parts;
+  return t < c + 1 ? c + 1 : t;
+}
 
-  num_splits[0] = 0;
-  int part = 0;
-  int b = 0, pg = 0, touched = 0;  // next unit; parts that already touched sequence b
-  while (part < num_parts && b < batch) {
-    const bool last = (part == num_parts - 1);
-    const int start_b = b, start_pg = pg, first_split = touched;
-    int end_b = b, end_pg = pg;
-    int64_t budget = target;
-    while (b < batch) {
-      const int units = seq_units(seqlens[b]);
-      const int rem = units - pg;
-      if (last || rem + c <= budget) {
-        budget -= rem + c;
-        num_splits[b + 1] = num_splits[b] + touched + 1;
-        end_b = b;
-        end_pg = units;
-        ++b;
-        pg = 0;
-        touched = 0;
-        if (!last && budget <= c) break;
-      } else {
-        const int64_t take = budget - c;
-        if (take >= 1) {
-          pg += (int)take;
-          ++touched;
-          end_b = b;
-          end_pg = pg;
-        }
-        break;
-      }
-    }
-    int32_t* md = tile_md + (int64_t)part * kTileMdInts;
-    md[0] = start_b;
-    md[1] = start_pg;
-    md[2] = end_b;
-    md[3] = end_pg;
-    md[4] = first_split;
-    md[5] = 0;
-    md[6] = 0;
-    md[7] = 0;
-    ++part;
+// Largest b in [0, batch) with prefix[b] <= x (prefix[0] = 0 <= x).
+MLA_HD inline int locate(const int64_t* prefix, int batch, int64_t x) {
+  int lo = 0, hi = batch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (prefix[mid] <= x)
+      lo = mid;
+    else
+      hi = mid - 1;
   }
-  for (; part < num_parts; ++part) {
-    int32_t* md = tile_md + (int64_t)part * kTileMdInts;
+  return lo;
+}
+
+// Part p's record from the prefix sums (prefix has batch + 1 entries).
+MLA_HD inline void plan_part(const int64_t* prefix, const int32_t* seqlens, int batch, int c, int64_t T,
+                             int p, int32_t* md) {
+  const int64_t W = prefix[batch];
+  const int64_t x = (int64_t)p * T;
+  for (int i = 0; i < kTileMdInts; ++i) md[i] = 0;
+  if (x >= W) {
     md[0] = batch;
-    md[1] = 0;
     md[2] = batch;
-    md[3] = 0;
-    md[4] = 0;
-    md[5] = 0;
-    md[6] = 0;
-    md[7] = 0;
+    return;
   }
+  const int b = locate(prefix, batch, x);
+  const int64_t off = x - prefix[b] - c;
+  const int pg = off > 0 ? (int)off : 0;
+  int eb, epg;
+  const int64_t xn = x + T;
+  if (xn >= W) {
+    eb = batch - 1;
+    epg = seq_units(seqlens[batch - 1]);
+  } else {
+    const int nb = locate(prefix, batch, xn);
+    const int64_t noff = xn - prefix[nb] - c;
+    if (noff > 0) {
+      eb = nb;
+      epg = (int)noff;
+    } else {
+      eb = nb - 1;
+      epg = seq_units(seqlens[nb - 1]);
+    }
+  }
+  md[0] = b;
+  md[1] = pg;
+  md[2] = eb;
+  md[3] = epg;
+  // parts before p that touched b: those from the one owning b's first page
+  md[4] = pg > 0 ? (int)(p - (prefix[b] + c) / T) : 0;
+}
+
+// Number of parts that touch sequence b.
+MLA_HD inline int32_t plan_touches(const int64_t* prefix, int b, int c, int64_t T) {
+  return (int32_t)((prefix[b + 1] - 1) / T - (prefix[b] + c) / T + 1);
+}
+
+// Host mirror (the device kernel computes the same with a parallel scan).
+inline void plan_split_kv_host(const int32_t* seqlens, int batch, int q_rows_per_kv_head, int num_parts,
+                               int32_t* tile_md, int32_t* num_splits, int64_t* prefix /* batch + 1 */) {
+  const int c = segment_cost(rows_per_block(q_rows_per_kv_head));
+  prefix[0] = 0;
+  for (int b = 0; b < batch; ++b) prefix[b + 1] = prefix[b] + c + seq_units(seqlens[b]);
+  const int64_t T = plan_stride(prefix[batch], num_parts, c);
+  for (int p = 0; p < num_parts; ++p) plan_part(prefix, seqlens, batch, c, T, p, tile_md + (int64_t)p * kTileMdInts);
+  num_splits[0] = 0;
+  for (int b = 0; b < batch; ++b) num_splits[b + 1] = num_splits[b] + plan_touches(prefix, b, c, T);
 }
 
 }  // namespace mla

@@ -199,3 +199,31 @@ def test_results_are_deterministic():
     a = run_gpu(inp)
     b = run_gpu(inp)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def ramp_scores(inp, per_token=0.125, q_value=4.0):
+    """Make scores grow along each sequence: q[..., 0] = q_value, k_t[0] = t * per_token.
+
+    With softmax_scale 1/sqrt(192) the score of token t is about 0.036 t (natural
+    units) on top of the random part, so the running max passes the kernel's
+    rescale slack several times over a few hundred tokens.
+    """
+    inp.q[..., 0] = q_value
+    for b in range(inp.block_table.shape[0]):
+        n = int(inp.cache_seqlens[b])
+        for t in range(n):
+            inp.k_storage[int(inp.block_table[b, t // 64]), t % 64, :, 0] = t * per_token
+    return inp
+
+
+@pytest.mark.parametrize("h_q,s_q,causal,parts", [(16, 1, False, 1), (32, 2, True, 2),
+                                                   (128, 1, False, 3), (128, 2, True, 1)])
+def test_growing_scores_exercise_the_rescale(h_q, s_q, causal, parts):
+    w = Workload("ramp", batch=2, s_q=s_q, h_q=h_q, causal=causal, seqlens="fixed",
+                 fixed_seqlens=(1500, 700))
+    inp = ramp_scores(draw(w, seed=8))
+    note(f"[parity] growing scores h_q={h_q} s_q={s_q} parts={parts}")
+    out, lse, _ = run_gpu(inp, num_parts=parts)
+    ref_out, ref_lse = oracle(inp)
+    assert float(ref_lse.max()) > 40.0  # far past several rescale thresholds
+    assert_parity(out, lse, ref_out, ref_lse, what="ramp")
