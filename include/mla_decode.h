@@ -164,7 +164,8 @@ typedef struct mla_decode_params {
  * Enqueue the decode (plan if needed, split-KV attention, lse merge) on `stream` and
  * return.  Alignment rules (MLA_ERR_BAD_STRIDE otherwise): q, k_cache and out 16-byte
  * aligned; q_*_stride, k_*_stride and out_*_stride multiples of 8 elements;
- * k_row_stride >= d; workspace 256-byte aligned.
+ * k_row_stride >= d; k_block_stride >= 63 * k_row_stride + d (a page's rows inside one
+ * block stride); workspace 256-byte aligned.
  */
 int mla_decode_with_kvcache(const mla_decode_params* params, void* stream);
 

@@ -30,20 +30,18 @@ int cu_count(int device) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WorkspaceLayout {
-  size_t tile_md, num_splits, part_lse, part_o, flush, total;
+  size_t tile_md, num_splits, part_lse, part_o, total;
 };
 
-// [plan][partial lse][partial O][flush scratch per decode workgroup]
+// [plan][partial lse][partial O]
 WorkspaceLayout layout(int64_t batch, int64_t rows, int64_t dv, int64_t num_parts) {
   WorkspaceLayout w;
   const int64_t slots = batch + num_parts;
-  const int64_t workgroups = num_parts * mla::row_blocks((int)rows);
   w.tile_md = 0;
   w.num_splits = align256((size_t)num_parts * mla::kTileMdInts * 4);
   w.part_lse = w.num_splits + align256((size_t)(batch + 1) * 4);
   w.part_o = w.part_lse + align256((size_t)(slots * rows) * 4);
-  w.flush = w.part_o + align256((size_t)(slots * rows * dv) * 4);
-  w.total = w.flush + align256((size_t)(workgroups * mla::kFlushFloatsPerWorkgroup) * 4);
+  w.total = w.part_o + align256((size_t)(slots * rows * dv) * 4);
   return w;
 }
 
@@ -157,6 +155,8 @@ int mla_decode_with_kvcache(const mla_decode_params* p, void* stream) {
       p->lse_batch_stride < 0 || p->lse_seq_stride < 0 || p->lse_head_stride < 0)
     return MLA_ERR_BAD_STRIDE;
   if (p->block_table_stride < p->max_blocks_per_seq) return MLA_ERR_BAD_STRIDE;
+  // a page's 64 rows lie inside one block stride (the copy reads rows 0..63 of a block)
+  if (p->k_block_stride < (int64_t)(p->block_size - 1) * p->k_row_stride + p->d) return MLA_ERR_BAD_STRIDE;
   if ((int64_t)64 * p->k_row_stride * 2 > INT32_MAX) return MLA_ERR_BAD_STRIDE;
   if ((int64_t)p->max_blocks_per_seq * 64 > INT32_MAX) return MLA_ERR_BAD_SHAPE;
 
@@ -212,7 +212,6 @@ int mla_decode_with_kvcache(const mla_decode_params* p, void* stream) {
   a.row_blocks = mla::row_blocks((int)rows);
   a.part_lse = (float*)(ws + w.part_lse);
   a.part_o = (float*)(ws + w.part_o);
-  a.flush = (float*)(ws + w.flush);
   a.out = (uint16_t*)p->out;
   a.o_sb = p->out_batch_stride;
   a.o_ss = p->out_seq_stride;

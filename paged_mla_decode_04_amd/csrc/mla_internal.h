@@ -22,15 +22,11 @@ struct DecodeArgs {
   int32_t num_parts, row_blocks;
   float* part_lse;             // [slots][rows]
   float* part_o;               // [slots][rows][512]
-  float* flush;                // per workgroup x 4 waves: carry + dump, 16 x 512 fp32 each
   uint16_t* out;               // bf16 bits
   int64_t o_sb, o_ss, o_sh;
   float* lse;
   int64_t l_sb, l_ss, l_sh;
 };
-
-// fp32 values of flush scratch per decode workgroup (4 waves x carry + dump of 16 x 512)
-constexpr int64_t kFlushFloatsPerWorkgroup = 4 * 2 * 16 * 512;
 
 hipError_t launch_plan(const int32_t* seqlens, int batch, int rows, int num_parts, int32_t* tile_md,
                        int32_t* num_splits, hipStream_t stream);

@@ -9,36 +9,29 @@
 // the work as (d + dv) multiply-adds per query-key pair and one d-element read
 // per cached token -- K and V come out of the same row, read once.
 //
-// Design on gfx950 (256 CUs, 160 KB LDS, 64-wide waves, bf16 MFMA):
-//   * one workgroup (4 waves) per CU processes one plan part: a contiguous
-//     run of 64-token pages, possibly spanning several sequences;
-//   * a page (64 x 576 bf16 = 72 KB) is copied HBM -> LDS with 16-byte
-//     buffer loads that write LDS directly (no VGPR staging), double
-//     buffered; all 4 waves issue the copies;
-//   * up to 4 compute waves own 16 or 32 query rows each (a workgroup holds
-//     at most 128 rows, so every page is read once for 128 heads); the query
-//     block stays in registers as MFMA operands and the fp32 output
-//     accumulator (up to 32 x 512 per wave) in the accumulation registers;
+// Design on gfx950 (256 CUs in 8 XCDs, 160 KB LDS, 64-wide waves, bf16 MFMA):
+//   * one workgroup (8 waves, 2 per SIMD) per CU processes one plan part for
+//     one block of up to 64 query rows: a contiguous run of 64-token pages,
+//     possibly spanning several sequences;
+//   * a page (64 x 576 bf16 = 72 KB) is copied HBM -> LDS with 16-byte buffer
+//     loads that write LDS directly (no register staging), double buffered;
 //   * scores are computed transposed, S^T = K . Q^T, on 16x16x32 bf16 MFMA,
-//     so every lane holds whole query rows: row max / row sum need only two
-//     cross-lane steps;
-//   * P . V is computed as O^T = V^T . P^T: P^T comes straight from the score
-//     registers (no data movement) and V^T from LDS with the gfx950
-//     transposing read ds_read_b64_tr_b16 (4 consecutive tokens per lane);
-//   * online softmax in the log2 domain.  The reference max only moves when a
-//     row's score exceeds it by more than 2^16; then (rarely) the wave flushes
-//     its unscaled accumulator into a carry in global scratch instead of
-//     rescaling it in registers, so no vector ALU op touches the accumulator
-//     inside the page loop;
+//     with the query tile held in registers, so every lane holds whole query
+//     rows and row max / row sum need two cross-lane steps;
+//   * P . V is computed as O^T = V^T . P^T; V^T comes from LDS through the
+//     gfx950 transposing read ds_read_b64_tr_b16 (4 consecutive tokens per
+//     lane), P^T through LDS in exactly the layout the scores leave it in;
+//   * online softmax in the log2 domain against a reference max per row that
+//     only moves when a page's max passes it by more than 2^16;
 //   * a part that covers only a piece of a sequence writes an fp32 partial
 //     (O / l, lse); the merge kernel combines them by lse (Flash-Decoding, as
 //     the Hacker News discussion of the FlashMLA release describes it).
 //
 // LDS page tile: 9 x 8 blocks of 1 KB; block (r, q) holds tokens 8r..8r+7 x
-// 16-byte chunks 8q..8q+7, token a of the block at 128 a, its chunk c at slot
-// (c % 8) ^ a ^ (r & 1).  The swizzle keeps both the 16-byte K reads (16
-// tokens x one chunk) and the 8-byte transposing V reads (4 tokens x 2 chunks
-// x 2 halves per 16 lanes) free of bank conflicts.
+// 16-byte chunks 8q..8q+7 (columns 64q..64q+63), token a of the block at
+// 128 a, its chunk c at slot (c % 8) ^ a ^ (r & 1).  The swizzle keeps both
+// the 16-byte K reads (16 tokens x one chunk) and the 8-byte transposing V
+// reads (4 tokens x 2 chunks x 2 halves per 16 lanes) free of bank conflicts.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -62,9 +55,7 @@ typedef __attribute__((address_space(3))) int32_t lds_i32;
 constexpr int kD = 576;
 constexpr int kDv = 512;
 constexpr int kPageBytes = 64 * kD * 2;  // 73728
-constexpr int kThreads = 256;
 constexpr int kKSteps = kD / 32;          // 18 MFMA k-steps of 32 for the scores
-constexpr int kColTiles = kDv / 16;       // 32 output column tiles of 16
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 16.0f;    // log2 units: p = 2^(x - m) stays <= 65536
@@ -84,12 +75,6 @@ __device__ __forceinline__ float wave_sum16(float v) {
   return v;
 }
 
-// Register-class hints (emit no instructions): the output accumulator lives
-// in the accumulation registers, scores in ordinary VGPRs, so that the query
-// fragments, scores and accumulator fit one wave's 512 registers.
-__device__ __forceinline__ void pin_acc(f32x4& x) { asm volatile("" : "+a"(x)); }
-__device__ __forceinline__ void pin_vgpr(f32x4& x) { asm volatile("" : "+v"(x)); }
-
 // Opaque copy of an LDS pointer: keeps base + constant address arithmetic from
 // being re-associated (and hoisted) so the constant lands in the instruction
 // offset field.
@@ -103,453 +88,444 @@ __device__ __forceinline__ lds_u8* launder(lds_u8* p) {
 // the next page's copies still in flight.
 __device__ __forceinline__ void block_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Nine 16-byte LDS-direct loads: chunk octets 0..8 of one token octet.  The
-// byte step between octets travels in the VGPR offset: the instruction's
-// immediate offset would move the LDS destination as well.
-template <int... Q>
-__device__ __forceinline__ void copy_row_octet(__amdgpu_buffer_rsrc_t rsrc, uint8_t* dst, uint32_t voff,
-                                               std::integer_sequence<int, Q...>) {
-  (__builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + 1024 * Q), 16, voff + 128u * Q, 0, 0, 0),
-   ...);
+// ---------------------------------------------------------------------------
+// Split-KV decode.
+//
+// One workgroup of 8 waves (2 per SIMD) handles one row block (up to 64 query
+// rows, NRT row tiles of 16) of one plan part.  Per page:
+//   scores   wave w computes S^T = K . Q^T for row tile w % NRT and 16-token
+//            tiles (w / NRT) * TT .. + TT - 1 (TT = 2 for 4 row tiles, else 1),
+//            keeping the query tile in registers;
+//   softmax  log2 domain, against a per-row reference max shared by the whole
+//            workgroup; p is rounded to bf16 and written to LDS already in
+//            the operand layout of the next product;
+//   values   wave w owns output columns 64 w .. 64 w + 63 for every row and
+//            accumulates O^T += V^T . P^T, reading V^T with the transposing
+//            LDS read.
+// Only wave w reads column block w of the values, so right after its own
+// products it may start the copy of the page two steps ahead into that block
+// (and into one rope block, free since the score step): the copy of the next
+// page is always in flight behind the arithmetic, with two barriers per page.
+//
+// Page bookkeeping runs three pages ahead on the scalar unit: the sequence
+// length and the block-table entry of a page are fetched one step before the
+// page's copy is issued, so no dependent load sits on the copy path.
+// ---------------------------------------------------------------------------
+
+constexpr int kThreads = 512;
+constexpr int kPOffset = 2 * kPageBytes;          // P^T operands: [row tile][32-token half][lane] x 16 B
+constexpr int kMaxOffset = kPOffset + 8 * 1024;   // page row max per (token group, row): f32 [4][64]
+constexpr int kSumOffset = kMaxOffset + 1024;     // row sums of rounded p per (token group, row)
+constexpr int kSumExOffset = kSumOffset + 1024;   // row sums of unrounded p per (token group, row)
+constexpr int kFlagOffset = kSumExOffset + 1024;  // per wave: a row max passed the reference
+constexpr int kSmemBytes = kFlagOffset + 8 * 4;
+static_assert(kSmemBytes <= 160 * 1024, "LDS budget");
+
+typedef const __attribute__((address_space(4))) int32_t cint32;  // read-only, uniform: scalar loads
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
+
+// 16-byte LDS-direct buffer load: lane l's 16 bytes land at lds_addr + 16 l.
+// Written as inline assembly so that the compiler does not track the LDS
+// write: it would otherwise make every later LDS read wait for all copies in
+// flight.  Completion is awaited explicitly (vmcnt) before the barrier that
+// hands a page over, and a copy only targets LDS that no wave reads any more.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr) : "memory");
 }
 
-// Copy one page's used rows into an LDS tile.  Wave w copies token octets 2w
-// and 2w+1 (18 x 1 KB).  Rows at or past `tokens` and pages outside the pool
-// read as zeros through the buffer range check, so no byte outside the cache
-// is touched and masked rows never carry stale NaNs.
-__device__ __forceinline__ void copy_page(const DecodeArgs& a, int phys, bool valid, int tokens,
-                                          uint8_t* tile, int wave, int lane) {
-  const uint8_t* base = a.k + (valid ? (int64_t)phys * a.k_block_bytes : 0);
-  const int32_t records = valid ? (int32_t)(64 * a.k_row_bytes) : 0;
-  __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, records, kBufferFlags);
-  const int ta = lane >> 3, e = lane & 7;
-#pragma unroll
-  for (int rr = 0; rr < 2; ++rr) {
-    const int r = 2 * wave + rr;
-    const int t = 8 * r + ta;
-    const uint32_t voff = (t < tokens)
-                              ? (uint32_t)(t * a.k_row_bytes + 16 * (e ^ ta ^ (r & 1)))
-                              : kOutOfRange;
-    copy_row_octet(rsrc, tile + 1024 * 9 * r, voff, std::make_integer_sequence<int, 9>{});
-  }
-}
-
-// Per-wave state.  A compute wave owns 16 query rows for the scores and the
-// softmax (lane row l % 16), and one column block of the output accumulator
-// for all the workgroup's rows: NWC row tiles x (32 / NWC) column tiles of
-// 16 x 16, always 128 accumulation registers.
-template <int NWC>
-struct WaveState {
-  static constexpr int kCT = kColTiles / NWC;  // column tiles of this wave's block
-  bf16x8 qf[kKSteps];       // Q^T operand fragments of the wave's 16 rows
-  f32x4 o[kCT][NWC];        // O^T accumulators: [column tile][row tile]
-  float m, l, le;           // own row: reference max (log2 units), sums of rounded /
-                            // unrounded probabilities
-  float cm, cl, cle;        // own row: the carry's reference and sums
-  bool carry;               // workgroup-uniform: the carry holds a flushed accumulator
+// Block table position of one page of the part and what is known about it.
+struct Cursor {
+  int seq, page;  // sequence, page within the sequence
+  int n;          // cached tokens of seq as stored (clamp_len applies the cap)
+  int phys;       // block-table entry (-1 past the row)
+  bool valid;     // inside the part
 };
 
-// Fold the accumulator into the carry: carry = carry * fc[row] + O (O unscaled),
-// then O = 0.  The accumulator is only stored (from the accumulation registers),
-// never operated on by vector ALU instructions, so the page loop keeps it in
-// AGPRs; the dump is read back as fresh values.
-template <int NWC>
-__device__ __forceinline__ void fold_into_carry(WaveState<NWC>& st, float* carry, float* dump, int lane,
-                                                const lds_f32* fc) {
-  constexpr int kCT = WaveState<NWC>::kCT;
-  constexpr int kStride = kCT * 16;
-  const int g = lane >> 4;
-#pragma unroll
-  for (int rt = 0; rt < NWC; ++rt)
-#pragma unroll
-    for (int ct = 0; ct < kCT; ++ct)
-      *(f32x4*)(dump + (16 * rt + (lane & 15)) * kStride + 16 * ct + 4 * g) = st.o[ct][rt];
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-#pragma unroll
-  for (int rt = 0; rt < NWC; ++rt) {
-    const float f = st.carry ? fc[16 * rt + (lane & 15)] : 0.f;
-#pragma unroll 2
-    for (int ct = 0; ct < kCT; ++ct) {
-      float* cp = carry + (16 * rt + (lane & 15)) * kStride + 16 * ct + 4 * g;
-      float* dp = dump + (16 * rt + (lane & 15)) * kStride + 16 * ct + 4 * g;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float d = __hip_atomic_load(dp + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const float c = st.carry ? __hip_atomic_load(cp + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.f;
-        __hip_atomic_store(cp + j, c * f + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-#pragma unroll
-    for (int ct = 0; ct < kCT; ++ct) {
-      st.o[ct][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      pin_acc(st.o[ct][rt]);
-    }
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+__device__ __forceinline__ int clamp_len(const DecodeArgs& a, int n) {
+  const int cap = a.max_blocks * kPageTokens;
+  return n < 0 ? 0 : (n > cap ? cap : n);
+}
+__device__ __forceinline__ int load_len(const DecodeArgs& a, int b) { return ((cint32*)a.seqlens)[b]; }
+__device__ __forceinline__ int load_phys(const DecodeArgs& a, int b, int page) {
+  return page < a.max_blocks ? ((cint32*)a.block_table)[(int64_t)b * a.bt_stride + page] : -1;
+}
+__device__ __forceinline__ int page_tokens(const DecodeArgs& a, const Cursor& c) {
+  if (!c.valid) return 0;
+  const int t = clamp_len(a, c.n) - kPageTokens * c.page;
+  return t > kPageTokens ? kPageTokens : t;
 }
 
-// LDS fragments are fetched a fixed number of steps ahead into explicit
-// register buffers, and consecutive MFMAs accumulate into different tiles, so
-// neither LDS latency nor the MFMA dependency chain is exposed; scheduling
-// barriers pin that order.
-constexpr int kAheadK = 2;  // score k-steps (4 fragments each)
-constexpr int kAheadV = 3;  // output column tiles (one transposed fragment each)
-
-// LDS regions next to the two page tiles.
-constexpr int kPFragOffset = 2 * kPageBytes;                   // P^T fragments [row tile][half][lane]
-constexpr int kStatsOffset = kPFragOffset + 4 * 2 * 64 * 16;   // fc / wo / wc [64 rows], flags[4]
-constexpr int kSmemBytes = kStatsOffset + 3 * 64 * 4 + 16;
-
-struct Lds {
-  lds_u8* base;
-  __device__ lds_bf16x8* pfrag(int rt, int half) const {
-    return (lds_bf16x8*)(base + kPFragOffset + (rt * 2 + half) * 1024);
-  }
-  __device__ lds_f32* fc() const { return (lds_f32*)(base + kStatsOffset); }
-  __device__ lds_f32* wo() const { return (lds_f32*)(base + kStatsOffset + 256); }
-  __device__ lds_f32* wc() const { return (lds_f32*)(base + kStatsOffset + 512); }
-  __device__ lds_i32* flags() const { return (lds_i32*)(base + kStatsOffset + 768); }
-};
-
-// One 64-token page for compute wave `wave`.  Scores and softmax for the
-// wave's own 16 rows; P^T fragments go through LDS to every compute wave;
-// each wave then adds V^T . P^T into its column block for all the rows.
-// `vis` is the own row's visible-token count relative to the page start.
-// Contains one workgroup barrier that the non-computing waves match with
-// page_barrier_for_idle().
-template <int NWC>
-__device__ __forceinline__ void compute_page(const DecodeArgs& a, WaveState<NWC>& st, const Lds& L, int wave,
-                                             int lane, int vis, lds_u8* kb0, lds_u8* kb1, lds_u8* const* vb,
-                                             float* carry, float* dump) {
-  constexpr int kCT = WaveState<NWC>::kCT;
-  const int g = lane >> 4;
-  // ---- scores of the own 16 rows: 4 token tiles, 18 k-steps
-  f32x4 s[4];
-#pragma unroll
-  for (int tt = 0; tt < 4; ++tt) s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  bf16x8 kf[kKSteps][4];
-  auto load_k = [&](int ks) {
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-      kf[ks][tt] = *(const lds_bf16x8*)(((ks & 1) ? kb1 : kb0) + 18432u * tt + 1024u * (ks >> 1));
-  };
-#pragma unroll
-  for (int ks = 0; ks < kAheadK; ++ks) load_k(ks);
-#pragma unroll
-  for (int ks = 0; ks < kKSteps; ++ks) {
-    if (ks + kAheadK < kKSteps) load_k(ks + kAheadK);
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-      s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks][tt], st.qf[ks], s[tt], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-#pragma unroll
-  for (int tt = 0; tt < 4; ++tt) pin_vgpr(s[tt]);
-
-  // ---- mask (token 16 tt + 4 g + j visible iff < vis), scale, row max
-  const int lim = vis - 4 * g;
-  float mx = -INFINITY;
-#pragma unroll
-  for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float x = (16 * tt + j < lim) ? s[tt][j] * a.scale_log2 : -INFINITY;
-      s[tt][j] = x;
-      mx = fmaxf(mx, x);
-    }
-  mx = wave_max16(mx);
-  // The reference max is set on the row's first visible key and moved only when
-  // a finite reference is exceeded by more than the slack; then the whole
-  // workgroup folds its accumulator into the carry (below).
-  const bool over = (st.m != -INFINITY) && (mx > st.m + kRescaleSlack);
-  const float fc = st.carry ? __builtin_amdgcn_exp2f(st.cm - st.m) : 0.f;  // carry factor at the old reference
-  const float m_new = over ? fmaxf(st.m, mx) : (st.m == -INFINITY ? mx : st.m);
-  // probabilities (bf16 P^T fragments per 32-token half) and their sums
-  const float mu = (m_new == -INFINITY) ? 0.f : m_new;
-  bf16x8 pf[2];
-  float sum = 0.f, sum_exact = 0.f;
-#pragma unroll
-  for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float e = __builtin_amdgcn_exp2f(s[tt][j] - mu);
-      const __bf16 p = (__bf16)e;
-      sum += (float)p;
-      sum_exact += e;
-      pf[tt >> 1][4 * (tt & 1) + j] = p;
-    }
-  sum = wave_sum16(sum);
-  sum_exact = wave_sum16(sum_exact);
-  L.pfrag(wave, 0)[lane] = pf[0];
-  L.pfrag(wave, 1)[lane] = pf[1];
-  if (g == 0) L.fc()[16 * wave + lane] = fc;
-  const bool wave_over = __builtin_amdgcn_ballot_w64(over) != 0;
-  if (lane == 0) L.flags()[wave] = wave_over ? 1 : 0;
-  block_sync();
-
-  bool flush = false;
-#pragma unroll
-  for (int w = 0; w < NWC; ++w) flush |= L.flags()[w] != 0;
-  if (flush) {  // rare: fold everything accumulated so far into the carry
-    fold_into_carry<NWC>(st, carry, dump, lane, L.fc());
-    st.cl = st.cl * fc + st.l;
-    st.cle = st.cle * fc + st.le;
-    st.cm = st.m;
-    st.l = sum;
-    st.le = sum_exact;
-    st.carry = true;
+// The page after c in the part's (sequence, page) order.  Uses c.n, fetched a
+// step earlier; starts the fetch of the new page's length (on a sequence
+// change) and table entry.
+__device__ __forceinline__ Cursor next_page(const DecodeArgs& a, const Cursor& c, int seq_last, int page_end) {
+  Cursor d = c;
+  if (!c.valid) return d;
+  const int end = c.seq == seq_last ? page_end : seq_units(clamp_len(a, c.n));
+  if (c.page + 1 < end) {
+    d.page = c.page + 1;
+  } else if (c.seq < seq_last) {
+    d.seq = c.seq + 1;
+    d.page = 0;
+    d.n = load_len(a, d.seq);
   } else {
-    st.l += sum;
-    st.le += sum_exact;
+    d.valid = false;
+    return d;
   }
-  st.m = m_new;
-
-  // ---- O^T[column block] += V^T . P^T over both halves, all row tiles
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    bf16x8 pr[NWC];
-#pragma unroll
-    for (int rt = 0; rt < NWC; ++rt) pr[rt] = L.pfrag(rt, half)[lane];
-    bf16x8 vf[kCT];
-    auto load_v = [&](int ct) {
-      lds_u8* vp = vb[ct & 3] + 9216u * (4 * half) + 1024u * (ct >> 2);
-      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)vp);
-      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 2 * 9216u));
-      vf[ct] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    };
-#pragma unroll
-    for (int ct = 0; ct < kAheadV && ct < kCT; ++ct) load_v(ct);
-#pragma unroll
-    for (int ct = 0; ct < kCT; ++ct) {
-      if (ct + kAheadV < kCT) load_v(ct + kAheadV);
-#pragma unroll
-      for (int rt = 0; rt < NWC; ++rt) {
-        st.o[ct][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[ct], pr[rt], st.o[ct][rt], 0, 0, 0);
-        pin_acc(st.o[ct][rt]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
+  d.phys = load_phys(a, d.seq, d.page);
+  return d;
 }
 
-// Segment epilogue, in two steps around a workgroup barrier (which the idle
-// waves match): each row's owner turns its statistics (with the carry, if the
-// workgroup flushed) into output weights and the lse; then every compute wave
-// writes its column block of every row, as bf16 output or fp32 partial.
-template <int NWC>
-__device__ __forceinline__ void publish_row_weights(const DecodeArgs& a, const WaveState<NWC>& st, const Lds& L,
-                                                    int wave, int lane, int row, int b, bool bad, bool final_out,
-                                                    int slot) {
-  float M = st.m, fo = 1.f, fc = 0.f;
-  if (st.carry) {
-    M = fmaxf(st.cm, st.m);
-    fo = st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.m - M);
-    fc = st.cm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.cm - M);
+// Start this wave's share of the copy of page c into the tile at LDS address
+// `tile`: column block `wave` of every row (8 x 1 KB) and the rope block of
+// token octet `wave` (1 KB) -- 9 loads per wave, 72 KB per workgroup.  Rows at
+// or past the page's token count, and pages whose table entry lies outside
+// the pool, read as zeros through the buffer range check.
+__device__ __forceinline__ bool issue_copy(const DecodeArgs& a, const Cursor& c, uint32_t tile, int wave,
+                                           int lane) {
+  const int tok = page_tokens(a, c);
+  if (tok <= 0) return false;
+  const bool ok = c.phys >= 0 && c.phys < a.num_blocks;
+  const uint8_t* base = a.k + (ok ? (int64_t)c.phys * a.k_block_bytes : 0);
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)base, (short)0, ok ? (int32_t)(kPageTokens * a.k_row_bytes) : 0, kBufferFlags);
+  const int ta = lane >> 3, e = lane & 7;
+  const uint32_t rb = (uint32_t)a.k_row_bytes;
+  {
+    const int t = 8 * wave + ta;
+    const uint32_t voff = t < tok ? t * rb + 16u * (64 + (e ^ ta ^ (wave & 1))) : kOutOfRange;
+    lds_dma16(rsrc, voff, tile + 1024u * (9 * wave + 8));
   }
-  const float Lr = st.l * fo + st.cl * fc;
-  const float LE = st.le * fo + st.cle * fc;
-  float inv = Lr > 0.f ? 1.f / Lr : 0.f;
-  float lse = LE > 0.f ? (M + __builtin_amdgcn_logf(LE)) * kLn2 : -INFINITY;
-  if (bad) {
-    inv = __builtin_nanf("");
-    lse = __builtin_nanf("");
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int t = 8 * r + ta;
+    const uint32_t voff = t < tok ? t * rb + 16u * (8 * wave + (e ^ ta ^ (r & 1))) : kOutOfRange;
+    lds_dma16(rsrc, voff, tile + 1024u * (9 * r + wave));
   }
-  if ((lane >> 4) == 0) {
-    L.wo()[16 * wave + lane] = fo * inv;
-    L.wc()[16 * wave + lane] = fc * inv;
-    if (row < a.rows) {
-      const int qi = row / a.h_q, h = row - qi * a.h_q;
-      if (final_out)
-        a.lse[(int64_t)b * a.l_sb + (int64_t)qi * a.l_ss + (int64_t)h * a.l_sh] = lse;
-      else
-        a.part_lse[(int64_t)slot * a.rows + row] = lse;
-    }
-  }
+  return true;
 }
 
-template <int NWC>
-__device__ __forceinline__ void write_block(const DecodeArgs& a, const WaveState<NWC>& st, const Lds& L,
-                                            const float* carry, int wave, int lane, int blk_row0, int b,
-                                            bool final_out, int slot) {
-  constexpr int kCT = WaveState<NWC>::kCT;
-  constexpr int kStride = kCT * 16;
-  const int g = lane >> 4;
-#pragma unroll
-  for (int rt = 0; rt < NWC; ++rt) {
-    const int r = blk_row0 + 16 * rt + (lane & 15);
-    const float wo = L.wo()[16 * rt + (lane & 15)];
-    const float wc = L.wc()[16 * rt + (lane & 15)];
-    const bool ok = r < a.rows;
-    const int rr = ok ? r : 0;
-    const int qi = rr / a.h_q, h = rr - qi * a.h_q;
-    const int col0 = wave * kCT * 16 + 4 * g;
-    const float* cp = carry + (16 * rt + (lane & 15)) * kStride + 4 * g;
-    if (final_out) {
-      uint16_t* op = a.out + (int64_t)b * a.o_sb + (int64_t)qi * a.o_ss + (int64_t)h * a.o_sh + col0;
-#pragma unroll
-      for (int ct = 0; ct < kCT; ++ct) {
-        f32x4 v = st.o[ct][rt] * wo;
-        if (st.carry) v += *(const f32x4*)(cp + 16 * ct) * wc;
-        const bf16x4 w = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-        if (ok) *(bf16x4*)(op + 16 * ct) = w;
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    } else {
-      float* pp = a.part_o + ((int64_t)slot * a.rows + rr) * kDv + col0;
-#pragma unroll
-      for (int ct = 0; ct < kCT; ++ct) {
-        f32x4 v = st.o[ct][rt] * wo;
-        if (st.carry) v += *(const f32x4*)(cp + 16 * ct) * wc;
-        if (ok) *(f32x4*)(pp + 16 * ct) = v;
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  }
-}
+constexpr int kAheadK = 3;  // score k-steps whose K fragments are read ahead
 
-// NWC compute waves (16 rows each for the scores, one column block each for
-// the output); all 4 waves copy pages.
-template <int NWC>
+template <int NRT>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmemBytes];
+  constexpr int TT = NRT == 4 ? 2 : 1;  // 16-token score tiles per scoring wave
+  constexpr int NG = 4 / TT;            // token groups a row's scores are split into
   const int wave = uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int g = lane >> 4;
-  constexpr int kBlockRows = NWC * 16;
-  constexpr int kCT = WaveState<NWC>::kCT;
+  const int g = lane >> 4, r16 = lane & 15;
 
-  // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a contiguous run
-  // of parts so neighbouring pieces of one sequence share that XCD's L2.
+  // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a contiguous
+  // run of (part, row block) pairs so that the row blocks of one part, and
+  // neighbouring parts of one sequence, share that XCD's L2.
   const int G = gridDim.x, hw = blockIdx.x;
   const int xcd = hw & 7, pos = hw >> 3;
   const int logical = xcd * (G >> 3) + min(xcd, G & 7) + pos;
   const int part = logical / a.row_blocks;
   const int mblock = logical - part * a.row_blocks;
 
-  const int32_t* md = a.tile_md + (int64_t)part * kTileMdInts;
-  const int seq_begin = uniform(md[0]);
+  cint32* md = (cint32*)a.tile_md + (int64_t)part * kTileMdInts;
+  const int seq_begin = md[0];
   if (seq_begin >= a.batch) return;
-  const int page_begin = uniform(md[1]);
-  const int seq_last = uniform(md[2]);
-  const int page_end = uniform(md[3]);
-  const int split_first = uniform(md[4]);
+  const int page_begin = md[1];
+  const int seq_last = md[2];
+  const int page_end = md[3];
+  const int split_first = md[4];
 
-  // per-lane LDS offsets (see the tile layout above)
-  const int kt = lane & 15;
-  const int ka = kt & 7, kr = kt >> 3;
-  const uint32_t kx = (uint32_t)(g ^ ka ^ (kr & 1));
-  const uint32_t kb_lane = 9216u * kr + 128u * ka;
-  const int vs = lane & 15;
-  const int va = 4 * (g & 1) + (vs >> 2);
-  const int vR = (g >> 1) & 1;
-  const uint32_t vy = (uint32_t)(((vs & 3) >> 1) ^ va ^ vR);
-  // this wave's column block starts at column tile wave * kCT (a multiple of 4)
-  const uint32_t vb_lane = 9216u * (g >> 1) + 128u * va + 8u * (vs & 1) + 1024u * (wave * kCT / 4);
+  lds_u8* const lds = (lds_u8*)smem;
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
+  // this lane's row r16 in the per-row statistics: [token group][row tile][r16]
+  lds_f32* const stats = (lds_f32*)launder(lds + kMaxOffset + 4u * r16);
+  constexpr int kSumAt = (kSumOffset - kMaxOffset) / 4, kSumExAt = (kSumExOffset - kMaxOffset) / 4;
 
-  const bool computes = wave < NWC;
-  const int blk_row0 = mblock * kBlockRows;
-  const int own_row = blk_row0 + 16 * wave + (lane & 15);
-  // this wave's flush scratch: carry, then dump, 16 * NWC rows x its columns
-  float* carry = a.flush + ((int64_t)hw * 4 + wave) * (2 * 16 * kDv);
-  float* dump = carry + 16 * kDv;
-  const Lds L{(lds_u8*)smem};
-  WaveState<NWC> st;
+  // score role
+  const bool scorer = wave < NRT * NG;
+  const int rt1 = wave % NRT;
+  const int tg = wave / NRT;
+  const int blk_row0 = mblock * NRT * 16;
+  const int own_row = blk_row0 + 16 * rt1 + r16;
+  // per-lane LDS offsets in a page tile (layout at the top of this file)
+  const int ka = r16 & 7, kr = r16 >> 3;
+  const uint32_t kx = (uint32_t)(g ^ ka ^ kr);
+  const uint32_t k_lane = 9216u * kr + 128u * ka + 18432u * (tg * TT);
+  const int va = 4 * (g & 1) + (r16 >> 2);
+  const uint32_t vy = (uint32_t)(((r16 & 3) >> 1) ^ va ^ ((g >> 1) & 1));
+  const uint32_t v_lane = 9216u * (g >> 1) + 128u * va + 8u * (r16 & 1) + 1024u * wave;
+  lds_u8* const pfrag = launder(lds + kPOffset + 16u * lane);
 
-  for (int b = seq_begin; b <= seq_last; ++b) {
-    int n = uniform(a.seqlens[b]);
-    n = n < 0 ? 0 : n;
-    const int cap = a.max_blocks * 64;
-    n = n > cap ? cap : n;
-    const int units = seq_units(n);
-    const int pb = (b == seq_begin) ? page_begin : 0;
-    const int pe = (b == seq_last) ? page_end : units;
-    const int split = (b == seq_begin) ? split_first : 0;
-    const int nsplit = uniform(a.num_splits[b + 1] - a.num_splits[b]);
-    const int slot = uniform(a.num_splits[b]) + split;
-    const int32_t* table = a.block_table + (int64_t)b * a.bt_stride;
+  bf16x8 qf[kKSteps];
+  f32x4 o[NRT][4];
+  float mref[NRT];           // reference max of row 16 rt + r16 (log2 units)
+  float m_own = -INFINITY;   // mref of the scoring row
+  float lsum = 0.f, lex = 0.f;
+  int lim = 0;               // visible tokens of the scoring row
+  bool bad = false;
+  int slot = 0, nsplit = 1;
 
-    if (computes) {
+  auto begin_segment = [&](const Cursor& c) {
+    const int b = c.seq;
+    const int n = clamp_len(a, c.n);
+    const int split = b == seq_begin ? split_first : 0;
+    const int s0 = ((cint32*)a.num_splits)[b];
+    slot = s0 + split;
+    nsplit = ((cint32*)a.num_splits)[b + 1] - s0;
+    if (scorer) {
       const bool ok = own_row < a.rows;
       const int rr = ok ? own_row : 0;
-      const uint16_t* qp = a.q + (int64_t)b * a.q_sb + (int64_t)(rr / a.h_q) * a.q_ss +
-                           (int64_t)(rr % a.h_q) * a.q_sh + 8 * g;
+      const int qi = rr / a.h_q, h = rr - qi * a.h_q;
+      lim = ok ? (a.causal ? n - (a.s_q - 1 - qi) : n) : 0;
+      const uint16_t* qp = a.q + (int64_t)b * a.q_sb + (int64_t)qi * a.q_ss + (int64_t)h * a.q_sh + 8 * g;
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) {
-        bf16x8 v = *(const bf16x8*)(qp + 32 * ks);
-        if (!ok) v = bf16x8{};
-        st.qf[ks] = v;
+        const bf16x8 v = *(const bf16x8*)(qp + 32 * ks);
+        qf[ks] = ok ? v : bf16x8{};
       }
-      st.m = -INFINITY;
-      st.l = 0.f;
-      st.le = 0.f;
-      st.cm = -INFINITY;
-      st.cl = 0.f;
-      st.cle = 0.f;
-      st.carry = false;
-#pragma unroll
-      for (int rt = 0; rt < NWC; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < kCT; ++ct) {
-          st.o[ct][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-          pin_acc(st.o[ct][rt]);
-        }
+      // wait for the queries here, before the next copy is issued, so that no
+      // later wait for them also waits for that copy
+      asm volatile("" ::"v"(qf[kKSteps - 1]), "v"(qf[0]));
     }
-    // visible keys of the own row: n, or n - (s_q - 1 - i) for query token i
-    const int vis_row = a.causal ? n - (a.s_q - 1 - own_row / a.h_q) : n;
-    bool bad = false;
-    // page p has tokens [64 p, min(64 p + 64, n)); pages with none are skipped
-    auto page_tokens = [&](int p) { int t = n - 64 * p; return t > 64 ? 64 : t; };
-    auto page_phys = [&](int p) { return uniform(table[p]); };
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      mref[rt] = -INFINITY;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) o[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    m_own = -INFINITY;
+    lsum = 0.f;
+    lex = 0.f;
+    bad = false;
+  };
 
-    int buf = 0;
-    bool pending = false;
-    if (pb < pe && page_tokens(pb) > 0) {
-      const int phys = page_phys(pb);
-      const bool valid = phys >= 0 && phys < a.num_blocks;
-      bad |= !valid;
-      copy_page(a, phys, valid, page_tokens(pb), smem, wave, lane);
-      pending = true;
-    }
-    for (int p = pb; p < pe; ++p) {
-      const int tok = page_tokens(p);
-      bool next = false;
-      if (p + 1 < pe && page_tokens(p + 1) > 0) {
-        const int phys = page_phys(p + 1);
-        const bool valid = phys >= 0 && phys < a.num_blocks;
-        bad |= !valid;
-        copy_page(a, phys, valid, page_tokens(p + 1), smem + (buf ^ 1) * kPageBytes, wave, lane);
-        next = true;
-      }
-      if (next)
-        __builtin_amdgcn_s_waitcnt(0x4F72);  // vmcnt(18): this page's copies have landed
-      else
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-      block_sync();
-      if (tok > 0 && pending) {
-        if (computes) {
-          // per-page base addresses; every access adds a constant that fits the
-          // LDS instruction's 16-bit offset field
-          lds_u8* tile = (lds_u8*)smem + buf * kPageBytes;
-          lds_u8* vb[4];
+  // ---- prologue: copies of the first two pages, queries of the first segment
+  Cursor c0;
+  c0.seq = seq_begin;
+  c0.page = page_begin;
+  c0.n = load_len(a, seq_begin);
+  c0.phys = load_phys(a, seq_begin, page_begin);
+  c0.valid = true;
+  issue_copy(a, c0, lds_addr, wave, lane);
+  Cursor c1 = next_page(a, c0, seq_last, page_end);
+  issue_copy(a, c1, lds_addr + kPageBytes, wave, lane);
+  begin_segment(c0);  // waits for the queries, and with them for both copies
+  bool c1_copy = false;
+  Cursor c2 = next_page(a, c1, seq_last, page_end);
+
+  for (int s = 0;; ++s) {
+    // ---- B1: page s (buffer s & 1) has landed; page s + 1 may be in flight
+    if (c1_copy)
+      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    block_sync();
+    const Cursor c3 = next_page(a, c2, seq_last, page_end);
+
+    const int tok0 = page_tokens(a, c0);
+    const uint32_t tile_off = (uint32_t)(s & 1) * kPageBytes;
+    lds_u8* const tile = lds + tile_off;
+    if (tok0 > 0) {
+      bad |= !(c0.phys >= 0 && c0.phys < a.num_blocks);
+      f32x4 sc[TT];
+      float psum = 0.f, psumx = 0.f;
+      if (scorer) {
+        // ---- scores of row tile rt1, token tiles tg * TT .. (16 x 16 per tile)
 #pragma unroll
-          for (int u = 0; u < 4; ++u) vb[u] = launder(tile + vb_lane + 16u * (vy ^ (2u * u)));
-          compute_page<NWC>(a, st, L, wave, lane, vis_row - 64 * p, launder(tile + kb_lane + 16u * kx),
-                            launder(tile + kb_lane + 16u * (kx ^ 4u)), vb, carry, dump);
+        for (int u = 0; u < TT; ++u) sc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        lds_u8* const kb0 = launder(tile + k_lane + 16u * kx);
+        lds_u8* const kb1 = launder(tile + k_lane + 16u * (kx ^ 4u));
+        bf16x8 kf[kKSteps][TT];
+        auto load_k = [&](int ks) {
+#pragma unroll
+          for (int u = 0; u < TT; ++u)
+            kf[ks][u] = *(const lds_bf16x8*)(((ks & 1) ? kb1 : kb0) + 18432u * u + 1024u * (ks >> 1));
+        };
+#pragma unroll
+        for (int ks = 0; ks < kAheadK; ++ks) load_k(ks);
+#pragma unroll
+        for (int ks = 0; ks < kKSteps; ++ks) {
+          if (ks + kAheadK < kKSteps) load_k(ks + kAheadK);
+#pragma unroll
+          for (int u = 0; u < TT; ++u)
+            sc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks][u], qf[ks], sc[u], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // ---- mask, scale, page row max; token 16 (tg TT + u) + 4 g + j
+        const int vis = lim - kPageTokens * c0.page - 16 * tg * TT - 4 * g;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < TT; ++u)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float x = (16 * u + j < vis) ? sc[u][j] * a.scale_log2 : -INFINITY;
+            sc[u][j] = x;
+            mx = fmaxf(mx, x);
+          }
+        mx = wave_max16(mx);
+        const bool over = mx > m_own + kRescaleSlack;
+        const float mu = m_own == -INFINITY ? 0.f : m_own;
+        // probabilities against the current reference (recomputed below if
+        // any row of the workgroup passed its reference)
+        bf16x8 pv;
+#pragma unroll
+        for (int u = 0; u < TT; ++u)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float e = __builtin_amdgcn_exp2f(sc[u][j] - mu);
+            const __bf16 p = (__bf16)e;
+            psum += (float)p;
+            psumx += e;
+            pv[4 * u + j] = p;
+          }
+        if constexpr (TT == 2) {
+          *(lds_bf16x8*)(pfrag + 1024u * (2 * rt1 + tg)) = pv;
         } else {
-          block_sync();  // matches the P hand-off barrier inside compute_page
+          *(lds_bf16x4*)(pfrag + 1024u * (2 * rt1 + (tg >> 1)) + 8u * (tg & 1)) =
+              bf16x4{pv[0], pv[1], pv[2], pv[3]};
+        }
+        if (g == 0) stats[64 * tg + 16 * rt1] = mx;
+        const bool wave_over = __builtin_amdgcn_ballot_w64(over) != 0;
+        if (lane == 0) ((lds_i32*)(lds + kFlagOffset))[wave] = wave_over ? 1 : 0;
+      } else if (lane == 0) {
+        ((lds_i32*)(lds + kFlagOffset))[wave] = 0;
+      }
+      block_sync();  // ---- B2: P, page row maxima and flags visible
+
+      const i32x4 f0 = *(const lds_i32x4*)(lds + kFlagOffset);
+      const i32x4 f1 = *(const lds_i32x4*)(lds + kFlagOffset + 16);
+      const i32x4 fo = f0 | f1;
+      const int any = uniform(fo[0] | fo[1] | fo[2] | fo[3]);
+      if (any) {
+        // Rare: some row's page max passed its reference by more than the
+        // slack (always on a segment's first page).  Every row moves its
+        // reference to max(reference, page max) and rescales what it has
+        // accumulated; the scorers redo their probabilities.
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+          float m_new = mref[rt];
+#pragma unroll
+          for (int gi = 0; gi < NG; ++gi) m_new = fmaxf(m_new, stats[64 * gi + 16 * rt]);
+          const float f = mref[rt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mref[rt] - m_new);
+          mref[rt] = m_new;
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) o[rt][ct] *= f;
+          if (scorer && rt == rt1) {
+            lsum *= f;
+            lex *= f;
+            m_own = m_new;
+          }
+        }
+        if (scorer) {
+          const float mu = m_own == -INFINITY ? 0.f : m_own;
+          bf16x8 pv;
+          psum = 0.f;
+          psumx = 0.f;
+#pragma unroll
+          for (int u = 0; u < TT; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float e = __builtin_amdgcn_exp2f(sc[u][j] - mu);
+              const __bf16 p = (__bf16)e;
+              psum += (float)p;
+              psumx += e;
+              pv[4 * u + j] = p;
+            }
+          if constexpr (TT == 2) {
+            *(lds_bf16x8*)(pfrag + 1024u * (2 * rt1 + tg)) = pv;
+          } else {
+            *(lds_bf16x4*)(pfrag + 1024u * (2 * rt1 + (tg >> 1)) + 8u * (tg & 1)) =
+                bf16x4{pv[0], pv[1], pv[2], pv[3]};
+          }
+        }
+        block_sync();  // ---- B3: redone P visible
+      }
+      lsum += psum;
+      lex += psumx;
+
+      // ---- O^T[column block wave] += V^T . P^T, both 32-token halves
+      lds_u8* vb[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) vb[ct] = launder(tile + v_lane + 16u * ((2u * ct) ^ vy));
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        bf16x8 pf[NRT];
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) pf[rt] = *(const lds_bf16x8*)(pfrag + 1024u * (2 * rt + kb));
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb[ct] + 36864u * kb));
+          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb[ct] + 36864u * kb + 18432u));
+          const bf16x8 vf = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+          for (int rt = 0; rt < NRT; ++rt)
+            o[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rt], o[rt][ct], 0, 0, 0);
         }
       }
-      block_sync();
-      pending = next;
-      buf ^= 1;
     }
 
-    if (computes) publish_row_weights<NWC>(a, st, L, wave, lane, own_row, b, bad, nsplit == 1, slot);
-    block_sync();
-    if (computes) write_block<NWC>(a, st, L, carry, wave, lane, blk_row0, b, nsplit == 1, slot);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    block_sync();
+    // ---- segment epilogue after its last page
+    const bool seg_last = !c1.valid || c1.seq != c0.seq;
+    if (seg_last) {
+      if (scorer) {
+        const float l = wave_sum16(lsum), le = wave_sum16(lex);
+        if (g == 0) {
+          stats[kSumAt + 64 * tg + 16 * rt1] = l;
+          stats[kSumExAt + 64 * tg + 16 * rt1] = le;
+        }
+      }
+      block_sync();  // ---- E1: row sums visible
+      const int b = c0.seq;
+      const bool final_out = nsplit == 1;
+      // opaque copy: keeps the output address arithmetic inside this rarely
+      // taken block instead of hoisted (and held in registers) across the loop
+      int row0 = blk_row0 + r16;
+      asm volatile("" : "+v"(row0));
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        float L = 0.f, LE = 0.f;
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+          L += stats[kSumAt + 64 * gi + 16 * rt];
+          LE += stats[kSumExAt + 64 * gi + 16 * rt];
+        }
+        float inv = L > 0.f ? 1.f / L : 0.f;
+        float lse = LE > 0.f ? (mref[rt] + __builtin_amdgcn_logf(LE)) * kLn2 : -INFINITY;
+        if (bad) {
+          inv = __builtin_nanf("");
+          lse = __builtin_nanf("");
+        }
+        const int row = row0 + 16 * rt;
+        if (row < a.rows) {
+          const int qi = row / a.h_q, h = row - qi * a.h_q;
+          const int col0 = 64 * wave + 4 * g;
+          if (final_out) {
+            uint16_t* op = a.out + (int64_t)b * a.o_sb + (int64_t)qi * a.o_ss + (int64_t)h * a.o_sh + col0;
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+              const f32x4 v = o[rt][ct] * inv;
+              *(bf16x4*)(op + 16 * ct) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+            }
+            if (wave == 0 && g == 0) a.lse[(int64_t)b * a.l_sb + (int64_t)qi * a.l_ss + (int64_t)h * a.l_sh] = lse;
+          } else {
+            float* pp = a.part_o + ((int64_t)slot * a.rows + row) * kDv + col0;
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) *(f32x4*)(pp + 16 * ct) = o[rt][ct] * inv;
+            if (wave == 0 && g == 0) a.part_lse[(int64_t)slot * a.rows + row] = lse;
+          }
+        }
+      }
+      if (c1.valid) begin_segment(c1);
+    }
+
+    // ---- copy page s + 2 into this page's buffer: this wave's value block
+    // and rope block are no longer read by anyone (the rope block since B2,
+    // the value block since this wave's own products above)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    c1_copy = issue_copy(a, c2, lds_addr + tile_off, wave, lane);
+    c0 = c1;
+    c1 = c2;
+    c2 = c3;
+    if (!c0.valid) break;
   }
 }
 

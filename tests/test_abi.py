@@ -108,6 +108,7 @@ BAD = [
     ("odd out stride", dict(out_head_stride=514), _lib.MLA_ERR_BAD_STRIDE),
     ("negative lse stride", dict(lse_head_stride=-1), _lib.MLA_ERR_BAD_STRIDE),
     ("table stride", dict(block_table_stride=3), _lib.MLA_ERR_BAD_STRIDE),
+    ("blocks overlap", dict(k_block_stride=63 * 576), _lib.MLA_ERR_BAD_STRIDE),
     ("plan without parts", dict(num_parts=0), _lib.MLA_ERR_BAD_SHAPE),
     ("workspace too small", dict(workspace_bytes=1024), _lib.MLA_ERR_WORKSPACE_TOO_SMALL),
 ]
@@ -149,11 +150,8 @@ def test_workspace_size_formula(lib):
         assert lib.mla_workspace_size(b, s_q, h_q, 1, 512, parts, ctypes.byref(n)) == _lib.MLA_OK
         rows = s_q * h_q
         slots = b + parts
-        rows_per_block = 16 if rows <= 16 else 32 if rows <= 32 else 64
-        workgroups = parts * -(-rows // rows_per_block)
-        flush = workgroups * 4 * 2 * 16 * 512 * 4   # per wave: carry + dump of 16 x 512 fp32
         want = (a256(parts * 8 * 4) + a256((b + 1) * 4) + a256(slots * rows * 4)
-                + a256(slots * rows * 512 * 4) + a256(flush))
+                + a256(slots * rows * 512 * 4))
         assert n.value == want
     assert lib.mla_workspace_size(2, 1, 16, 1, 512, 4, None) == _lib.MLA_ERR_NULL_POINTER
     assert lib.mla_workspace_size(2, 0, 16, 1, 512, 4, ctypes.byref(n)) == _lib.MLA_ERR_BAD_SHAPE
