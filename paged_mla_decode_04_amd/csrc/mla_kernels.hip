@@ -27,11 +27,12 @@
 //     (O / l, lse); the merge kernel combines them by lse (Flash-Decoding, as
 //     the Hacker News discussion of the FlashMLA release describes it).
 //
-// LDS page tile: 9 x 8 blocks of 1 KB; block (r, q) holds tokens 8r..8r+7 x
-// 16-byte chunks 8q..8q+7 (columns 64q..64q+63), token a of the block at
-// 128 a, its chunk c at slot (c % 8) ^ a ^ (r & 1).  The swizzle keeps both
-// the 16-byte K reads (16 tokens x one chunk) and the 8-byte transposing V
-// reads (4 tokens x 2 chunks x 2 halves per 16 lanes) free of bank conflicts.
+// LDS chunk tile (32 tokens): 9 x 4 blocks of 1 KB; block (r, q) holds tokens
+// 8r..8r+7 x 16-byte column chunks 8q..8q+7 (columns 64q..64q+63), token a of
+// the block at 128 a, its chunk c at slot (c % 8) ^ a ^ 2 (r & 1).  The swizzle
+// keeps both the 16-byte K reads (16 tokens x one chunk per 16 lanes, two
+// such groups per 512 bytes of banks) and the 8-byte transposing V reads
+// (4 tokens x 2 chunks x 2 halves per 16 lanes) free of bank conflicts.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -91,34 +92,48 @@ __device__ __forceinline__ void block_sync() { asm volatile("s_waitcnt lgkmcnt(0
 // ---------------------------------------------------------------------------
 // Split-KV decode.
 //
-// One workgroup of 8 waves (2 per SIMD) handles one row block (up to 64 query
-// rows, NRT row tiles of 16) of one plan part.  Per page:
-//   scores   wave w computes S^T = K . Q^T for row tile w % NRT and 16-token
-//            tiles (w / NRT) * TT .. + TT - 1 (TT = 2 for 4 row tiles, else 1),
-//            keeping the query tile in registers;
-//   softmax  log2 domain, against a per-row reference max shared by the whole
-//            workgroup; p is rounded to bf16 and written to LDS already in
-//            the operand layout of the next product;
-//   values   wave w owns output columns 64 w .. 64 w + 63 for every row and
-//            accumulates O^T += V^T . P^T, reading V^T with the transposing
-//            LDS read.
-// Only wave w reads column block w of the values, so right after its own
-// products it may start the copy of the page two steps ahead into that block
-// (and into one rope block, free since the score step): the copy of the next
-// page is always in flight behind the arithmetic, with two barriers per page.
+// One workgroup of 8 waves handles one row block (up to 64 query rows, NRT row
+// tiles of 16) of one plan part, stepping through its keys 32 tokens (half a
+// page) at a time.  Waves w and w + 4 share a SIMD; the roles are split so
+// that each SIMD always has matrix work from one wave while the other waits:
+//   score waves 0..3   wave i holds the queries of row tiles 2(i&1), 2(i&1)+1
+//                      (32 rows) and computes S^T = K . Q^T for token tile
+//                      i >> 1 (16 tokens) of a chunk: every 16-byte K read
+//                      from LDS feeds two MFMAs.  It then masks, scales and
+//                      exponentiates against the per-row reference max and
+//                      writes P (bf16) to LDS already in the operand layout of
+//                      the value product;
+//   value waves 4..7   wave 4 + j owns output columns 128 j .. 128 j + 127 of
+//                      all rows and accumulates O^T += V^T . P^T, reading V^T
+//                      with the transposing LDS read.
+// In step t the score waves work on chunk t + 1 while the value waves work on
+// chunk t, the copy of chunk t + 2 lands and that of chunk t + 3 is issued,
+// into four 36 KB chunk tiles; one workgroup barrier per step.
 //
-// Page bookkeeping runs three pages ahead on the scalar unit: the sequence
-// length and the block-table entry of a page are fetched one step before the
-// page's copy is issued, so no dependent load sits on the copy path.
+// Online softmax in the log2 domain: p = 2^(x - m) against a reference m per
+// row that only moves when a chunk's max passes it by more than 2^16.  The
+// score waves write P optimistically against the current reference together
+// with their per-lane chunk maxima and a flag; when a flag is set (a
+// segment's first chunk, and rarely later) every wave moves the reference of
+// its rows at the start of the next step, the value waves rescale their
+// accumulators and the score waves redo P from the scores they still hold,
+// behind one extra barrier.  No cross-lane reduction is needed otherwise.
+//
+// Page bookkeeping runs four chunks ahead on the scalar unit: the sequence
+// length and the block-table entry of a chunk are fetched a step before its
+// copy is issued, so no dependent load sits on the copy path.
 // ---------------------------------------------------------------------------
 
 constexpr int kThreads = 512;
-constexpr int kPOffset = 2 * kPageBytes;          // P^T operands: [row tile][32-token half][lane] x 16 B
-constexpr int kMaxOffset = kPOffset + 8 * 1024;   // page row max per (token group, row): f32 [4][64]
-constexpr int kSumOffset = kMaxOffset + 1024;     // row sums of rounded p per (token group, row)
-constexpr int kSumExOffset = kSumOffset + 1024;   // row sums of unrounded p per (token group, row)
-constexpr int kFlagOffset = kSumExOffset + 1024;  // per wave: a row max passed the reference
-constexpr int kSmemBytes = kFlagOffset + 8 * 4;
+constexpr int kChunk = 32;                            // tokens per pipeline step
+constexpr int kChunkBytes = kChunk * kD * 2;          // 36864
+constexpr int kBuffers = 4;                           // chunk tiles in LDS
+constexpr int kPOffset = kBuffers * kChunkBytes;      // P^T: [parity][row tile][lane] x 16 B
+constexpr int kCmaxOffset = kPOffset + 2 * 4096;      // chunk maxima: [parity][token tile][lane group][row] f32
+constexpr int kFlagOffset = kCmaxOffset + 2 * 2048;   // [parity][score wave] int
+constexpr int kFinalOffset = kFlagOffset + 2 * 4 * 4; // [parity] segment totals (below)
+constexpr int kFinalSum = 0, kFinalSumX = 128, kFinalRef = 256, kFinalFloats = 320;  // [2][64], [2][64], [64]
+constexpr int kSmemBytes = kFinalOffset + 2 * kFinalFloats * 4;
 static_assert(kSmemBytes <= 160 * 1024, "LDS budget");
 
 typedef const __attribute__((address_space(4))) int32_t cint32;  // read-only, uniform: scalar loads
@@ -129,17 +144,18 @@ typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
 // Written as inline assembly so that the compiler does not track the LDS
 // write: it would otherwise make every later LDS read wait for all copies in
 // flight.  Completion is awaited explicitly (vmcnt) before the barrier that
-// hands a page over, and a copy only targets LDS that no wave reads any more.
+// hands a chunk over, and a copy only targets a tile no wave reads any more.
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds_addr) {
   asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr) : "memory");
 }
 
-// Block table position of one page of the part and what is known about it.
+// One 32-token chunk of the part's (sequence, chunk) order.
 struct Cursor {
-  int seq, page;  // sequence, page within the sequence
-  int n;          // cached tokens of seq as stored (clamp_len applies the cap)
-  int phys;       // block-table entry (-1 past the row)
-  bool valid;     // inside the part
+  int seq, chunk;  // sequence, chunk within the sequence (page chunk / 2)
+  int n;           // cached tokens of seq as stored (clamp_len applies the cap)
+  int phys;        // block-table entry of the chunk's page (-1 past the row)
+  bool valid;      // inside the part
+  bool bad;        // the page lies outside the pool (known once the copy is issued)
 };
 
 __device__ __forceinline__ int clamp_len(const DecodeArgs& a, int n) {
@@ -150,72 +166,417 @@ __device__ __forceinline__ int load_len(const DecodeArgs& a, int b) { return ((c
 __device__ __forceinline__ int load_phys(const DecodeArgs& a, int b, int page) {
   return page < a.max_blocks ? ((cint32*)a.block_table)[(int64_t)b * a.bt_stride + page] : -1;
 }
-__device__ __forceinline__ int page_tokens(const DecodeArgs& a, const Cursor& c) {
+// chunks a sequence of n tokens occupies; an empty sequence owns one empty chunk
+__device__ __forceinline__ int chunk_count(int n) { return n <= 0 ? 1 : (n + kChunk - 1) / kChunk; }
+__device__ __forceinline__ int chunk_tokens(const DecodeArgs& a, const Cursor& c) {
   if (!c.valid) return 0;
-  const int t = clamp_len(a, c.n) - kPageTokens * c.page;
-  return t > kPageTokens ? kPageTokens : t;
+  const int t = clamp_len(a, c.n) - kChunk * c.chunk;
+  return t > kChunk ? kChunk : t;
 }
 
-// The page after c in the part's (sequence, page) order.  Uses c.n, fetched a
-// step earlier; starts the fetch of the new page's length (on a sequence
-// change) and table entry.
-__device__ __forceinline__ Cursor next_page(const DecodeArgs& a, const Cursor& c, int seq_last, int page_end) {
+// The chunk after c in the part.  Uses c.n, fetched at least a step earlier;
+// starts the fetch of a new sequence's length and of a new page's table entry.
+__device__ __forceinline__ Cursor next_chunk(const DecodeArgs& a, const Cursor& c, int seq_last, int page_end) {
   Cursor d = c;
+  d.bad = false;
   if (!c.valid) return d;
-  const int end = c.seq == seq_last ? page_end : seq_units(clamp_len(a, c.n));
-  if (c.page + 1 < end) {
-    d.page = c.page + 1;
+  int end = chunk_count(clamp_len(a, c.n));
+  if (c.seq == seq_last && 2 * page_end < end) end = 2 * page_end;
+  if (c.chunk + 1 < end) {
+    d.chunk = c.chunk + 1;
+    if ((d.chunk & 1) == 0) d.phys = load_phys(a, d.seq, d.chunk >> 1);
   } else if (c.seq < seq_last) {
     d.seq = c.seq + 1;
-    d.page = 0;
+    d.chunk = 0;
     d.n = load_len(a, d.seq);
+    d.phys = load_phys(a, d.seq, 0);
   } else {
     d.valid = false;
-    return d;
   }
-  d.phys = load_phys(a, d.seq, d.page);
   return d;
 }
 
-// Start this wave's share of the copy of page c into the tile at LDS address
-// `tile`: column block `wave` of every row (8 x 1 KB) and the rope block of
-// token octet `wave` (1 KB) -- 9 loads per wave, 72 KB per workgroup.  Rows at
-// or past the page's token count, and pages whose table entry lies outside
-// the pool, read as zeros through the buffer range check.
-__device__ __forceinline__ bool issue_copy(const DecodeArgs& a, const Cursor& c, uint32_t tile, int wave,
-                                           int lane) {
-  const int tok = page_tokens(a, c);
+// Start this wave's share of the copy of chunk c into the tile at LDS address
+// `tile`: value wave 4 + j copies column blocks 2j, 2j+1 (its own values) of
+// the chunk's 32 rows (8 x 1 KB), score wave i the rope block of token octet
+// i (1 KB).  Rows at or past the chunk's token count, and pages whose table
+// entry lies outside the pool, read as zeros through the buffer range check.
+// Returns whether loads were issued; sets c.bad for an entry outside the pool.
+__device__ __forceinline__ bool issue_copy(const DecodeArgs& a, Cursor& c, uint32_t tile, int wave, int lane) {
+  const int tok = chunk_tokens(a, c);
   if (tok <= 0) return false;
   const bool ok = c.phys >= 0 && c.phys < a.num_blocks;
-  const uint8_t* base = a.k + (ok ? (int64_t)c.phys * a.k_block_bytes : 0);
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)base, (short)0, ok ? (int32_t)(kPageTokens * a.k_row_bytes) : 0, kBufferFlags);
-  const int ta = lane >> 3, e = lane & 7;
+  c.bad = !ok;
   const uint32_t rb = (uint32_t)a.k_row_bytes;
-  {
+  const uint8_t* base = a.k + (ok ? (int64_t)c.phys * a.k_block_bytes + (int64_t)(c.chunk & 1) * kChunk * rb : 0);
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, ok ? (int32_t)(kChunk * rb) : 0, kBufferFlags);
+  const int ta = lane >> 3, e = lane & 7;
+  if (wave < 4) {
     const int t = 8 * wave + ta;
-    const uint32_t voff = t < tok ? t * rb + 16u * (64 + (e ^ ta ^ (wave & 1))) : kOutOfRange;
+    const uint32_t voff = t < tok ? t * rb + 16u * (64 + (e ^ ta ^ (2 * (wave & 1)))) : kOutOfRange;
     lds_dma16(rsrc, voff, tile + 1024u * (9 * wave + 8));
-  }
+  } else {
+    const int j = wave - 4;
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const int t = 8 * r + ta;
-    const uint32_t voff = t < tok ? t * rb + 16u * (8 * wave + (e ^ ta ^ (r & 1))) : kOutOfRange;
-    lds_dma16(rsrc, voff, tile + 1024u * (9 * r + wave));
+    for (int r = 0; r < 4; ++r) {
+      const int t = 8 * r + ta;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t voff = t < tok ? t * rb + 16u * (16 * j + 8 * h + (e ^ ta ^ (2 * (r & 1)))) : kOutOfRange;
+        lds_dma16(rsrc, voff, tile + 1024u * (9 * r + 2 * j + h));
+      }
+    }
   }
   return true;
 }
 
-constexpr int kAheadK = 3;  // score k-steps whose K fragments are read ahead
+constexpr int kAheadK = 6;  // score k-steps whose K fragment is read ahead
+
+// What a workgroup knows about its plan part.
+struct PartInfo {
+  int seq_begin, page_begin, seq_last, page_end, split_first;
+  int blk_row0;
+};
+
+// The decode loop of one role.  Both roles run the same cursor sequence and
+// meet the same workgroup barriers in the same order: every condition around a
+// barrier depends only on scalar bookkeeping shared by all waves or on flags
+// read from LDS after a barrier.  Each role has its own copy of the loop so
+// that the score state (queries) and the value state (accumulators) never
+// occupy registers at the same time.
+template <int NRT, bool SCORE>
+__device__ __forceinline__ void decode_role(const DecodeArgs& a, const PartInfo& pi, lds_u8* const lds,
+                                            const int wave, const int lane) {
+  const int g = lane >> 4, r16 = lane & 15;
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
+  lds_f32* const cmax = (lds_f32*)(lds + kCmaxOffset);
+  lds_i32* const flags = (lds_i32*)(lds + kFlagOffset);
+  lds_f32* const fin = (lds_f32*)(lds + kFinalOffset);
+  lds_u8* const plane = launder(lds + kPOffset + 16u * lane);
+
+  // ---- score role: rows 16 (rp0 + rt) + r16, token tile tt of each chunk
+  const int tt = (wave & 3) >> 1;
+  const int rp0 = 2 * (wave & 1);
+  const bool score_active = NRT == 4 || (wave & 1) == 0;
+  const int ka = r16 & 7, kr = r16 >> 3;
+  const uint32_t kx = (uint32_t)(g ^ ka ^ (2 * kr));
+  const uint32_t k_lane = 9216u * (2 * tt + kr) + 128u * ka;
+  bf16x8 qf[SCORE ? 2 : 1][kKSteps];
+  f32x4 sc[2];
+  float m_own[2] = {-INFINITY, -INFINITY};
+  float lsum[2] = {0.f, 0.f}, lsumx[2] = {0.f, 0.f};
+  float psum[2] = {0.f, 0.f}, psumx[2] = {0.f, 0.f};
+  int lim[2] = {0, 0};
+  // ---- value role: columns 128 vj .. 128 vj + 127 of rows 16 rt + r16
+  const int vj = wave & 3;
+  const int va = 4 * (g & 1) + (r16 >> 2);
+  const uint32_t vy = (uint32_t)(((r16 & 3) >> 1) ^ va ^ (2 * ((g >> 1) & 1)));
+  const uint32_t v_lane = 9216u * (g >> 1) + 1024u * (2 * vj) + 128u * va + 8u * (r16 & 1);
+  f32x4 o[SCORE ? 1 : NRT][8];
+  float mref[NRT];
+  if constexpr (!SCORE) {
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      mref[rt] = -INFINITY;
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) o[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  bool seg_bad = false;
+  int seg_slot = 0, seg_nsplit = 1;
+
+  // Load the queries of the segment of chunk c and reset the score state.
+  // Waits for the loads here, before the next copy is issued, so that no later
+  // wait for them also waits for that copy.
+  auto begin_score_segment = [&](const Cursor& c) {
+    if constexpr (SCORE) {
+      const int n = clamp_len(a, c.n);
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const int row = pi.blk_row0 + 16 * (rp0 + rt) + r16;
+        const bool ok = row < a.rows && rp0 + rt < NRT;
+        const int rr = ok ? row : 0;
+        const int qi = rr / a.h_q, h = rr - qi * a.h_q;
+        lim[rt] = ok ? (a.causal ? n - (a.s_q - 1 - qi) : n) : 0;
+        const uint16_t* qp = a.q + (int64_t)c.seq * a.q_sb + (int64_t)qi * a.q_ss + (int64_t)h * a.q_sh + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < kKSteps; ++ks) {
+          const bf16x8 v = *(const bf16x8*)(qp + 32 * ks);
+          qf[rt][ks] = ok ? v : bf16x8{};
+        }
+        m_own[rt] = -INFINITY;
+        lsum[rt] = 0.f;
+        lsumx[rt] = 0.f;
+      }
+      asm volatile("" ::"v"(qf[0][kKSteps - 1]), "v"(qf[1][kKSteps - 1]), "v"(qf[0][0]), "v"(qf[1][0]));
+    }
+  };
+
+  // ---- prologue: copies of chunks 0 and 1; queries of the first segment
+  Cursor S;  // chunk t + 1 (scores)
+  S.seq = pi.seq_begin;
+  S.chunk = 2 * pi.page_begin;
+  S.n = load_len(a, pi.seq_begin);
+  S.phys = load_phys(a, pi.seq_begin, pi.page_begin);
+  S.valid = true;
+  S.bad = false;
+  issue_copy(a, S, lds_addr, wave, lane);
+  Cursor L = next_chunk(a, S, pi.seq_last, pi.page_end);  // chunk t + 2 (landing)
+  issue_copy(a, L, lds_addr + kChunkBytes, wave, lane);
+  Cursor I = next_chunk(a, L, pi.seq_last, pi.page_end);  // chunk t + 3 (issued this step)
+  begin_score_segment(S);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  block_sync();
+  Cursor V;  // chunk t (values)
+  V.valid = false;
+  V.seq = -1;
+  V.bad = false;
+  V.chunk = 0;
+  V.n = 0;
+  V.phys = -1;
+  int p_seq = -1;  // chunk t - 1: its sequence, -1 if none
+  bool p_valid = false;
+
+  for (int t = -1;; ++t) {
+    const bool v_has = V.valid && chunk_tokens(a, V) > 0;
+    const bool epi = p_valid && (!V.valid || V.seq != p_seq);
+    if (!V.valid && !S.valid && !epi) break;
+    const Cursor N = next_chunk(a, I, pi.seq_last, pi.page_end);  // chunk t + 4: fetch its length / entry now
+    const int par = t & 1;
+
+    if constexpr (!SCORE) {
+      // ---- close the segment that ended with chunk t - 1
+      if (epi) {
+        const lds_f32* fs = fin + ((t - 1) & 1) * kFinalFloats + r16;
+        const bool final_out = seg_nsplit == 1;
+        int row0 = pi.blk_row0 + r16;  // opaque: keeps the address arithmetic in this block
+        asm volatile("" : "+v"(row0));
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+          const float L0 = fs[kFinalSum + 16 * rt] + fs[kFinalSum + 64 + 16 * rt];
+          const float LE = fs[kFinalSumX + 16 * rt] + fs[kFinalSumX + 64 + 16 * rt];
+          float inv = L0 > 0.f ? 1.f / L0 : 0.f;
+          float lse = LE > 0.f ? (fs[kFinalRef + 16 * rt] + __builtin_amdgcn_logf(LE)) * kLn2 : -INFINITY;
+          if (seg_bad) {
+            inv = __builtin_nanf("");
+            lse = __builtin_nanf("");
+          }
+          const int row = row0 + 16 * rt;
+          if (row < a.rows) {
+            const int qi = row / a.h_q, h = row - qi * a.h_q;
+            const int col0 = 128 * vj + 4 * g;
+            if (final_out) {
+              uint16_t* op = a.out + (int64_t)p_seq * a.o_sb + (int64_t)qi * a.o_ss + (int64_t)h * a.o_sh + col0;
+#pragma unroll
+              for (int ct = 0; ct < 8; ++ct) {
+                const f32x4 v = o[rt][ct] * inv;
+                *(bf16x4*)(op + 16 * ct) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+              }
+              if (vj == 0 && g == 0)
+                a.lse[(int64_t)p_seq * a.l_sb + (int64_t)qi * a.l_ss + (int64_t)h * a.l_sh] = lse;
+            } else {
+              float* pp = a.part_o + ((int64_t)seg_slot * a.rows + row) * kDv + col0;
+#pragma unroll
+              for (int ct = 0; ct < 8; ++ct) *(f32x4*)(pp + 16 * ct) = o[rt][ct] * inv;
+              if (vj == 0 && g == 0) a.part_lse[(int64_t)seg_slot * a.rows + row] = lse;
+            }
+          }
+#pragma unroll
+          for (int ct = 0; ct < 8; ++ct) o[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+          mref[rt] = -INFINITY;
+        }
+      }
+      if (V.valid && (!p_valid || V.seq != p_seq)) {  // the values enter a new segment
+        const int split = V.seq == pi.seq_begin ? pi.split_first : 0;
+        const int s0 = ((cint32*)a.num_splits)[V.seq];
+        seg_slot = s0 + split;
+        seg_nsplit = ((cint32*)a.num_splits)[V.seq + 1] - s0;
+        seg_bad = false;
+      }
+    }
+
+    // ---- chunk t's flags: move the reference max where a chunk max passed it
+    if (v_has) {
+      const i32x4 fl = *(const lds_i32x4*)(flags + 4 * par);
+      if (uniform(fl[0] | fl[1] | fl[2] | fl[3])) {
+        const lds_f32* cm = cmax + par * 512 + r16;
+        if constexpr (SCORE) {
+          if (score_active) {
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+              const int rw = 16 * (rp0 + rt);
+              float m_new = m_own[rt];
+#pragma unroll
+              for (int gi = 0; gi < 8; ++gi) m_new = fmaxf(m_new, cm[64 * gi + rw]);
+              const float f = m_own[rt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_own[rt] - m_new);
+              lsum[rt] *= f;
+              lsumx[rt] *= f;
+              m_own[rt] = m_new;
+              const float mu = m_new == -INFINITY ? 0.f : m_new;
+              bf16x4 pv;
+              psum[rt] = 0.f;
+              psumx[rt] = 0.f;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const float e = __builtin_amdgcn_exp2f(sc[rt][j] - mu);
+                const __bf16 p = (__bf16)e;
+                psum[rt] += (float)p;
+                psumx[rt] += e;
+                pv[j] = p;
+              }
+              *(lds_bf16x4*)(plane + par * 4096 + 1024u * (rp0 + rt) + 8u * tt) = pv;
+            }
+          }
+        } else {
+#pragma unroll
+          for (int rt = 0; rt < NRT; ++rt) {
+            float m_new = mref[rt];
+#pragma unroll
+            for (int gi = 0; gi < 8; ++gi) m_new = fmaxf(m_new, cm[64 * gi + 16 * rt]);
+            const float f = mref[rt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mref[rt] - m_new);
+            mref[rt] = m_new;
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) o[rt][ct] *= f;
+          }
+        }
+        block_sync();  // ---- redone P visible
+      }
+    }
+
+    if constexpr (SCORE) {
+      // ---- chunk t's probabilities are final: add their sums
+      if (v_has) {
+        lsum[0] += psum[0];
+        lsum[1] += psum[1];
+        lsumx[0] += psumx[0];
+        lsumx[1] += psumx[1];
+      }
+      // ---- chunk t ended its segment: publish the row totals
+      if (V.valid && (!S.valid || S.seq != V.seq) && score_active) {
+        lds_f32* fs = fin + par * kFinalFloats;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          const float l = wave_sum16(lsum[rt]), lx = wave_sum16(lsumx[rt]);
+          const int rw = 16 * (rp0 + rt) + r16;
+          if (g == 0) {
+            fs[kFinalSum + 64 * tt + rw] = l;
+            fs[kFinalSumX + 64 * tt + rw] = lx;
+            if (tt == 0) fs[kFinalRef + rw] = m_own[rt];
+          }
+        }
+      }
+      // ---- chunk t + 1 starts a segment: its queries
+      if (S.valid && V.valid && S.seq != V.seq) begin_score_segment(S);
+    }
+
+    // ---- copy chunk t + 3 into the tile chunk t - 1 used
+    const bool issued = issue_copy(a, I, lds_addr + (uint32_t)((t + 3) & 3) * kChunkBytes, wave, lane);
+
+    if constexpr (SCORE) {
+      if (score_active && S.valid && chunk_tokens(a, S) > 0) {
+        // ---- scores of chunk t + 1: 32 rows x 16 tokens, two MFMAs per K read
+        lds_u8* const tile = lds + (uint32_t)((t + 1) & 3) * kChunkBytes;
+        lds_u8* const kb0 = launder(tile + k_lane + 16u * kx);
+        lds_u8* const kb1 = launder(tile + k_lane + 16u * (kx ^ 4u));
+        sc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        bf16x8 kf[kKSteps];
+#pragma unroll
+        for (int ks = 0; ks < kAheadK; ++ks) kf[ks] = *(const lds_bf16x8*)(((ks & 1) ? kb1 : kb0) + 1024u * (ks >> 1));
+#pragma unroll
+        for (int ks = 0; ks < kKSteps; ++ks) {
+          if (ks + kAheadK < kKSteps)
+            kf[ks + kAheadK] =
+                *(const lds_bf16x8*)((((ks + kAheadK) & 1) ? kb1 : kb0) + 1024u * ((ks + kAheadK) >> 1));
+          sc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[0][ks], sc[0], 0, 0, 0);
+          sc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[1][ks], sc[1], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // ---- mask, scale; token 32 chunk + 16 tt + 4 g + j
+        const int base_tok = kChunk * S.chunk + 16 * tt + 4 * g;
+        const int par1 = (t + 1) & 1;
+        bool over = false;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          const int vis = lim[rt] - base_tok;
+          float mx = -INFINITY;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float x = j < vis ? sc[rt][j] * a.scale_log2 : -INFINITY;
+            sc[rt][j] = x;
+            mx = fmaxf(mx, x);
+          }
+          over |= mx > m_own[rt] + kRescaleSlack;
+          cmax[par1 * 512 + 64 * (4 * tt + g) + 16 * (rp0 + rt) + r16] = mx;
+          const float mu = m_own[rt] == -INFINITY ? 0.f : m_own[rt];
+          bf16x4 pv;
+          psum[rt] = 0.f;
+          psumx[rt] = 0.f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float e = __builtin_amdgcn_exp2f(sc[rt][j] - mu);
+            const __bf16 p = (__bf16)e;
+            psum[rt] += (float)p;
+            psumx[rt] += e;
+            pv[j] = p;
+          }
+          *(lds_bf16x4*)(plane + par1 * 4096 + 1024u * (rp0 + rt) + 8u * tt) = pv;
+        }
+        const bool wave_over = __builtin_amdgcn_ballot_w64(over) != 0;
+        if (lane == 0) flags[4 * par1 + wave] = wave_over ? 1 : 0;
+      } else if (lane == 0) {
+        flags[4 * ((t + 1) & 1) + wave] = 0;
+      }
+    } else {
+      if (V.valid) seg_bad |= V.bad;
+      if (v_has) {
+        // ---- O^T[columns 128 vj ..] += V^T . P^T for chunk t
+        lds_u8* const tile = lds + (uint32_t)(t & 3) * kChunkBytes;
+        lds_u8* vb[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) vb[u] = launder(tile + v_lane + 16u * ((2u * u) ^ vy));
+        bf16x8 pf[NRT];
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) pf[rt] = *(const lds_bf16x8*)(plane + par * 4096 + 1024u * rt);
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb[ct & 3] + 1024u * (ct >> 2)));
+          const bf16x4 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb[ct & 3] + 1024u * (ct >> 2) + 18432u));
+          const bf16x8 vf = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+          for (int rt = 0; rt < NRT; ++rt)
+            o[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rt], o[rt][ct], 0, 0, 0);
+        }
+      }
+    }
+
+    // ---- end of step: this wave's share of chunk t + 2 has landed and all
+    // LDS reads of the step have returned
+    if (issued) {
+      if constexpr (SCORE)
+        asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    block_sync();
+    p_seq = V.seq;
+    p_valid = V.valid;
+    V = S;
+    S = L;
+    L = I;
+    I = N;
+  }
+}
 
 template <int NRT>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmemBytes];
-  constexpr int TT = NRT == 4 ? 2 : 1;  // 16-token score tiles per scoring wave
-  constexpr int NG = 4 / TT;            // token groups a row's scores are split into
   const int wave = uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int g = lane >> 4, r16 = lane & 15;
 
   // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a contiguous
   // run of (part, row block) pairs so that the row blocks of one part, and
@@ -227,306 +588,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   const int mblock = logical - part * a.row_blocks;
 
   cint32* md = (cint32*)a.tile_md + (int64_t)part * kTileMdInts;
-  const int seq_begin = md[0];
-  if (seq_begin >= a.batch) return;
-  const int page_begin = md[1];
-  const int seq_last = md[2];
-  const int page_end = md[3];
-  const int split_first = md[4];
-
+  PartInfo pi;
+  pi.seq_begin = md[0];
+  if (pi.seq_begin >= a.batch) return;
+  pi.page_begin = md[1];
+  pi.seq_last = md[2];
+  pi.page_end = md[3];
+  pi.split_first = md[4];
+  pi.blk_row0 = mblock * NRT * 16;
   lds_u8* const lds = (lds_u8*)smem;
-  const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
-  // this lane's row r16 in the per-row statistics: [token group][row tile][r16]
-  lds_f32* const stats = (lds_f32*)launder(lds + kMaxOffset + 4u * r16);
-  constexpr int kSumAt = (kSumOffset - kMaxOffset) / 4, kSumExAt = (kSumExOffset - kMaxOffset) / 4;
-
-  // score role
-  const bool scorer = wave < NRT * NG;
-  const int rt1 = wave % NRT;
-  const int tg = wave / NRT;
-  const int blk_row0 = mblock * NRT * 16;
-  const int own_row = blk_row0 + 16 * rt1 + r16;
-  // per-lane LDS offsets in a page tile (layout at the top of this file)
-  const int ka = r16 & 7, kr = r16 >> 3;
-  const uint32_t kx = (uint32_t)(g ^ ka ^ kr);
-  const uint32_t k_lane = 9216u * kr + 128u * ka + 18432u * (tg * TT);
-  const int va = 4 * (g & 1) + (r16 >> 2);
-  const uint32_t vy = (uint32_t)(((r16 & 3) >> 1) ^ va ^ ((g >> 1) & 1));
-  const uint32_t v_lane = 9216u * (g >> 1) + 128u * va + 8u * (r16 & 1) + 1024u * wave;
-  lds_u8* const pfrag = launder(lds + kPOffset + 16u * lane);
-
-  bf16x8 qf[kKSteps];
-  f32x4 o[NRT][4];
-  float mref[NRT];           // reference max of row 16 rt + r16 (log2 units)
-  float m_own = -INFINITY;   // mref of the scoring row
-  float lsum = 0.f, lex = 0.f;
-  int lim = 0;               // visible tokens of the scoring row
-  bool bad = false;
-  int slot = 0, nsplit = 1;
-
-  auto begin_segment = [&](const Cursor& c) {
-    const int b = c.seq;
-    const int n = clamp_len(a, c.n);
-    const int split = b == seq_begin ? split_first : 0;
-    const int s0 = ((cint32*)a.num_splits)[b];
-    slot = s0 + split;
-    nsplit = ((cint32*)a.num_splits)[b + 1] - s0;
-    if (scorer) {
-      const bool ok = own_row < a.rows;
-      const int rr = ok ? own_row : 0;
-      const int qi = rr / a.h_q, h = rr - qi * a.h_q;
-      lim = ok ? (a.causal ? n - (a.s_q - 1 - qi) : n) : 0;
-      const uint16_t* qp = a.q + (int64_t)b * a.q_sb + (int64_t)qi * a.q_ss + (int64_t)h * a.q_sh + 8 * g;
-#pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) {
-        const bf16x8 v = *(const bf16x8*)(qp + 32 * ks);
-        qf[ks] = ok ? v : bf16x8{};
-      }
-      // wait for the queries here, before the next copy is issued, so that no
-      // later wait for them also waits for that copy
-      asm volatile("" ::"v"(qf[kKSteps - 1]), "v"(qf[0]));
-    }
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      mref[rt] = -INFINITY;
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) o[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    m_own = -INFINITY;
-    lsum = 0.f;
-    lex = 0.f;
-    bad = false;
-  };
-
-  // ---- prologue: copies of the first two pages, queries of the first segment
-  Cursor c0;
-  c0.seq = seq_begin;
-  c0.page = page_begin;
-  c0.n = load_len(a, seq_begin);
-  c0.phys = load_phys(a, seq_begin, page_begin);
-  c0.valid = true;
-  issue_copy(a, c0, lds_addr, wave, lane);
-  Cursor c1 = next_page(a, c0, seq_last, page_end);
-  issue_copy(a, c1, lds_addr + kPageBytes, wave, lane);
-  begin_segment(c0);  // waits for the queries, and with them for both copies
-  bool c1_copy = false;
-  Cursor c2 = next_page(a, c1, seq_last, page_end);
-
-  for (int s = 0;; ++s) {
-    // ---- B1: page s (buffer s & 1) has landed; page s + 1 may be in flight
-    if (c1_copy)
-      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    block_sync();
-    const Cursor c3 = next_page(a, c2, seq_last, page_end);
-
-    const int tok0 = page_tokens(a, c0);
-    const uint32_t tile_off = (uint32_t)(s & 1) * kPageBytes;
-    lds_u8* const tile = lds + tile_off;
-    if (tok0 > 0) {
-      bad |= !(c0.phys >= 0 && c0.phys < a.num_blocks);
-      f32x4 sc[TT];
-      float psum = 0.f, psumx = 0.f;
-      if (scorer) {
-        // ---- scores of row tile rt1, token tiles tg * TT .. (16 x 16 per tile)
-#pragma unroll
-        for (int u = 0; u < TT; ++u) sc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-        lds_u8* const kb0 = launder(tile + k_lane + 16u * kx);
-        lds_u8* const kb1 = launder(tile + k_lane + 16u * (kx ^ 4u));
-        bf16x8 kf[kKSteps][TT];
-        auto load_k = [&](int ks) {
-#pragma unroll
-          for (int u = 0; u < TT; ++u)
-            kf[ks][u] = *(const lds_bf16x8*)(((ks & 1) ? kb1 : kb0) + 18432u * u + 1024u * (ks >> 1));
-        };
-#pragma unroll
-        for (int ks = 0; ks < kAheadK; ++ks) load_k(ks);
-#pragma unroll
-        for (int ks = 0; ks < kKSteps; ++ks) {
-          if (ks + kAheadK < kKSteps) load_k(ks + kAheadK);
-#pragma unroll
-          for (int u = 0; u < TT; ++u)
-            sc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks][u], qf[ks], sc[u], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        // ---- mask, scale, page row max; token 16 (tg TT + u) + 4 g + j
-        const int vis = lim - kPageTokens * c0.page - 16 * tg * TT - 4 * g;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int u = 0; u < TT; ++u)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float x = (16 * u + j < vis) ? sc[u][j] * a.scale_log2 : -INFINITY;
-            sc[u][j] = x;
-            mx = fmaxf(mx, x);
-          }
-        mx = wave_max16(mx);
-        const bool over = mx > m_own + kRescaleSlack;
-        const float mu = m_own == -INFINITY ? 0.f : m_own;
-        // probabilities against the current reference (recomputed below if
-        // any row of the workgroup passed its reference)
-        bf16x8 pv;
-#pragma unroll
-        for (int u = 0; u < TT; ++u)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float e = __builtin_amdgcn_exp2f(sc[u][j] - mu);
-            const __bf16 p = (__bf16)e;
-            psum += (float)p;
-            psumx += e;
-            pv[4 * u + j] = p;
-          }
-        if constexpr (TT == 2) {
-          *(lds_bf16x8*)(pfrag + 1024u * (2 * rt1 + tg)) = pv;
-        } else {
-          *(lds_bf16x4*)(pfrag + 1024u * (2 * rt1 + (tg >> 1)) + 8u * (tg & 1)) =
-              bf16x4{pv[0], pv[1], pv[2], pv[3]};
-        }
-        if (g == 0) stats[64 * tg + 16 * rt1] = mx;
-        const bool wave_over = __builtin_amdgcn_ballot_w64(over) != 0;
-        if (lane == 0) ((lds_i32*)(lds + kFlagOffset))[wave] = wave_over ? 1 : 0;
-      } else if (lane == 0) {
-        ((lds_i32*)(lds + kFlagOffset))[wave] = 0;
-      }
-      block_sync();  // ---- B2: P, page row maxima and flags visible
-
-      const i32x4 f0 = *(const lds_i32x4*)(lds + kFlagOffset);
-      const i32x4 f1 = *(const lds_i32x4*)(lds + kFlagOffset + 16);
-      const i32x4 fo = f0 | f1;
-      const int any = uniform(fo[0] | fo[1] | fo[2] | fo[3]);
-      if (any) {
-        // Rare: some row's page max passed its reference by more than the
-        // slack (always on a segment's first page).  Every row moves its
-        // reference to max(reference, page max) and rescales what it has
-        // accumulated; the scorers redo their probabilities.
-#pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) {
-          float m_new = mref[rt];
-#pragma unroll
-          for (int gi = 0; gi < NG; ++gi) m_new = fmaxf(m_new, stats[64 * gi + 16 * rt]);
-          const float f = mref[rt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mref[rt] - m_new);
-          mref[rt] = m_new;
-#pragma unroll
-          for (int ct = 0; ct < 4; ++ct) o[rt][ct] *= f;
-          if (scorer && rt == rt1) {
-            lsum *= f;
-            lex *= f;
-            m_own = m_new;
-          }
-        }
-        if (scorer) {
-          const float mu = m_own == -INFINITY ? 0.f : m_own;
-          bf16x8 pv;
-          psum = 0.f;
-          psumx = 0.f;
-#pragma unroll
-          for (int u = 0; u < TT; ++u)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float e = __builtin_amdgcn_exp2f(sc[u][j] - mu);
-              const __bf16 p = (__bf16)e;
-              psum += (float)p;
-              psumx += e;
-              pv[4 * u + j] = p;
-            }
-          if constexpr (TT == 2) {
-            *(lds_bf16x8*)(pfrag + 1024u * (2 * rt1 + tg)) = pv;
-          } else {
-            *(lds_bf16x4*)(pfrag + 1024u * (2 * rt1 + (tg >> 1)) + 8u * (tg & 1)) =
-                bf16x4{pv[0], pv[1], pv[2], pv[3]};
-          }
-        }
-        block_sync();  // ---- B3: redone P visible
-      }
-      lsum += psum;
-      lex += psumx;
-
-      // ---- O^T[column block wave] += V^T . P^T, both 32-token halves
-      lds_u8* vb[4];
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) vb[ct] = launder(tile + v_lane + 16u * ((2u * ct) ^ vy));
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        bf16x8 pf[NRT];
-#pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) pf[rt] = *(const lds_bf16x8*)(pfrag + 1024u * (2 * rt + kb));
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb[ct] + 36864u * kb));
-          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb[ct] + 36864u * kb + 18432u));
-          const bf16x8 vf = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-          for (int rt = 0; rt < NRT; ++rt)
-            o[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rt], o[rt][ct], 0, 0, 0);
-        }
-      }
-    }
-
-    // ---- segment epilogue after its last page
-    const bool seg_last = !c1.valid || c1.seq != c0.seq;
-    if (seg_last) {
-      if (scorer) {
-        const float l = wave_sum16(lsum), le = wave_sum16(lex);
-        if (g == 0) {
-          stats[kSumAt + 64 * tg + 16 * rt1] = l;
-          stats[kSumExAt + 64 * tg + 16 * rt1] = le;
-        }
-      }
-      block_sync();  // ---- E1: row sums visible
-      const int b = c0.seq;
-      const bool final_out = nsplit == 1;
-      // opaque copy: keeps the output address arithmetic inside this rarely
-      // taken block instead of hoisted (and held in registers) across the loop
-      int row0 = blk_row0 + r16;
-      asm volatile("" : "+v"(row0));
-#pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) {
-        float L = 0.f, LE = 0.f;
-#pragma unroll
-        for (int gi = 0; gi < NG; ++gi) {
-          L += stats[kSumAt + 64 * gi + 16 * rt];
-          LE += stats[kSumExAt + 64 * gi + 16 * rt];
-        }
-        float inv = L > 0.f ? 1.f / L : 0.f;
-        float lse = LE > 0.f ? (mref[rt] + __builtin_amdgcn_logf(LE)) * kLn2 : -INFINITY;
-        if (bad) {
-          inv = __builtin_nanf("");
-          lse = __builtin_nanf("");
-        }
-        const int row = row0 + 16 * rt;
-        if (row < a.rows) {
-          const int qi = row / a.h_q, h = row - qi * a.h_q;
-          const int col0 = 64 * wave + 4 * g;
-          if (final_out) {
-            uint16_t* op = a.out + (int64_t)b * a.o_sb + (int64_t)qi * a.o_ss + (int64_t)h * a.o_sh + col0;
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct) {
-              const f32x4 v = o[rt][ct] * inv;
-              *(bf16x4*)(op + 16 * ct) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-            }
-            if (wave == 0 && g == 0) a.lse[(int64_t)b * a.l_sb + (int64_t)qi * a.l_ss + (int64_t)h * a.l_sh] = lse;
-          } else {
-            float* pp = a.part_o + ((int64_t)slot * a.rows + row) * kDv + col0;
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct) *(f32x4*)(pp + 16 * ct) = o[rt][ct] * inv;
-            if (wave == 0 && g == 0) a.part_lse[(int64_t)slot * a.rows + row] = lse;
-          }
-        }
-      }
-      if (c1.valid) begin_segment(c1);
-    }
-
-    // ---- copy page s + 2 into this page's buffer: this wave's value block
-    // and rope block are no longer read by anyone (the rope block since B2,
-    // the value block since this wave's own products above)
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    c1_copy = issue_copy(a, c2, lds_addr + tile_off, wave, lane);
-    c0 = c1;
-    c1 = c2;
-    c2 = c3;
-    if (!c0.valid) break;
-  }
+  if (wave < 4)
+    decode_role<NRT, true>(a, pi, lds, wave, lane);
+  else
+    decode_role<NRT, false>(a, pi, lds, wave, lane);
 }
 
 // Merge the partials of every sequence that more than one part touched:
