@@ -50,11 +50,16 @@ def build(verbose: bool = False) -> str:
         elif verbose and text.strip():
             print(text)
     if failed:
+        # never leave a library built from older sources next to failed ones
+        if os.path.exists(LIB_PATH):
+            os.remove(LIB_PATH)
         raise RuntimeError("hipcc failed:\n" + "\n".join(failed))
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
     if r.returncode != 0:
+        if os.path.exists(LIB_PATH):
+            os.remove(LIB_PATH)
         raise RuntimeError("link failed:\n" + r.stdout.decode(errors="replace"))
     os.replace(tmp, LIB_PATH)
     for o in objs:

@@ -133,7 +133,8 @@ constexpr int kCmaxOffset = kPOffset + 2 * 4096;      // chunk maxima: [parity][
 constexpr int kFlagOffset = kCmaxOffset + 2 * 2048;   // [parity][score wave] int
 constexpr int kFinalOffset = kFlagOffset + 2 * 4 * 4; // [parity] segment totals (below)
 constexpr int kFinalSum = 0, kFinalSumX = 128, kFinalRef = 256, kFinalFloats = 320;  // [2][64], [2][64], [64]
-constexpr int kSmemBytes = kFinalOffset + 2 * kFinalFloats * 4;
+constexpr int kRingOffset = kFinalOffset + 2 * kFinalFloats * 4;  // 8 chunk descriptors x 16 B
+constexpr int kSmemBytes = kRingOffset + 8 * 16;
 static_assert(kSmemBytes <= 160 * 1024, "LDS budget");
 
 typedef const __attribute__((address_space(4))) int32_t cint32;  // read-only, uniform: scalar loads
@@ -149,13 +150,13 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t 
   asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr) : "memory");
 }
 
-// One 32-token chunk of the part's (sequence, chunk) order.
+// Position of the page-bookkeeping cursor: one 32-token chunk of the part's
+// (sequence, chunk) order.
 struct Cursor {
   int seq, chunk;  // sequence, chunk within the sequence (page chunk / 2)
   int n;           // cached tokens of seq as stored (clamp_len applies the cap)
   int phys;        // block-table entry of the chunk's page (-1 past the row)
   bool valid;      // inside the part
-  bool bad;        // the page lies outside the pool (known once the copy is issued)
 };
 
 __device__ __forceinline__ int clamp_len(const DecodeArgs& a, int n) {
@@ -168,17 +169,11 @@ __device__ __forceinline__ int load_phys(const DecodeArgs& a, int b, int page) {
 }
 // chunks a sequence of n tokens occupies; an empty sequence owns one empty chunk
 __device__ __forceinline__ int chunk_count(int n) { return n <= 0 ? 1 : (n + kChunk - 1) / kChunk; }
-__device__ __forceinline__ int chunk_tokens(const DecodeArgs& a, const Cursor& c) {
-  if (!c.valid) return 0;
-  const int t = clamp_len(a, c.n) - kChunk * c.chunk;
-  return t > kChunk ? kChunk : t;
-}
 
 // The chunk after c in the part.  Uses c.n, fetched at least a step earlier;
 // starts the fetch of a new sequence's length and of a new page's table entry.
 __device__ __forceinline__ Cursor next_chunk(const DecodeArgs& a, const Cursor& c, int seq_last, int page_end) {
   Cursor d = c;
-  d.bad = false;
   if (!c.valid) return d;
   int end = chunk_count(clamp_len(a, c.n));
   if (c.seq == seq_last && 2 * page_end < end) end = 2 * page_end;
@@ -196,42 +191,87 @@ __device__ __forceinline__ Cursor next_chunk(const DecodeArgs& a, const Cursor& 
   return d;
 }
 
-// Start this wave's share of the copy of chunk c into the tile at LDS address
-// `tile`: value wave 4 + j copies column blocks 2j, 2j+1 (its own values) of
-// the chunk's 32 rows (8 x 1 KB), score wave i the rope block of token octet
-// i (1 KB).  Rows at or past the chunk's token count, and pages whose table
-// entry lies outside the pool, read as zeros through the buffer range check.
-// Returns whether loads were issued; sets c.bad for an entry outside the pool.
-__device__ __forceinline__ bool issue_copy(const DecodeArgs& a, Cursor& c, uint32_t tile, int wave, int lane) {
-  const int tok = chunk_tokens(a, c);
-  if (tok <= 0) return false;
-  const bool ok = c.phys >= 0 && c.phys < a.num_blocks;
-  c.bad = !ok;
+// What every wave needs to know about one chunk.  Wave 0 walks the part with a
+// Cursor and publishes these, five chunks ahead, in a ring of eight LDS slots
+// (16 bytes each), so that the page bookkeeping costs the CU's scalar unit one
+// wave's work instead of eight.
+struct Chunk {
+  int seq;     // -1: past the end of the part
+  int chunk;   // within the sequence
+  int tok;     // tokens in the chunk (0 for an empty sequence's chunk)
+  int phys;    // block-table entry of its page
+  bool first;  // first chunk of its segment (the part's piece of one sequence)
+  bool last;   // last chunk of its segment
+  bool bad;    // the entry lies outside the pool
+  __device__ bool valid() const { return seq >= 0; }
+};
+
+__device__ __forceinline__ i32x4 pack_chunk(const DecodeArgs& a, const Cursor& c, const Cursor& next, bool first) {
+  i32x4 d;
+  if (!c.valid) {
+    d = i32x4{-1, 0, 0, -1};
+    return d;
+  }
+  int tok = clamp_len(a, c.n) - kChunk * c.chunk;
+  tok = tok < 0 ? 0 : (tok > kChunk ? kChunk : tok);
+  const bool last = !next.valid || next.seq != c.seq;
+  const bool bad = tok > 0 && !(c.phys >= 0 && c.phys < a.num_blocks);
+  d = i32x4{c.seq, c.chunk, tok | (first ? 256 : 0) | (last ? 512 : 0) | (bad ? 1024 : 0), c.phys};
+  return d;
+}
+
+__device__ __forceinline__ Chunk unpack_chunk(const i32x4 d) {
+  Chunk c;
+  c.seq = uniform(d[0]);
+  c.chunk = uniform(d[1]);
+  const int z = uniform(d[2]);
+  c.phys = uniform(d[3]);
+  c.tok = z & 255;
+  c.first = (z & 256) != 0;
+  c.last = (z & 512) != 0;
+  c.bad = (z & 1024) != 0;
+  return c;
+}
+
+// Source of one chunk's copy: a buffer resource over the chunk's 32 rows
+// (zero records for a page outside the pool, so it reads as zeros); rows at
+// or past the chunk's token count read as zeros through the range check.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const DecodeArgs& a, const Chunk& c) {
+  const bool ok = !c.bad;
   const uint32_t rb = (uint32_t)a.k_row_bytes;
-  const uint8_t* base = a.k + (ok ? (int64_t)c.phys * a.k_block_bytes + (int64_t)(c.chunk & 1) * kChunk * rb : 0);
-  const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, ok ? (int32_t)(kChunk * rb) : 0, kBufferFlags);
+  const uint64_t base =
+      (uint64_t)(a.k + (ok ? (int64_t)c.phys * a.k_block_bytes + (int64_t)(c.chunk & 1) * kChunk * rb : 0));
+  // the descriptor fields are wave-uniform; say so, so the resource lands in scalar registers
+  const uint64_t ubase = ((uint64_t)(uint32_t)uniform((int)(base >> 32)) << 32) | (uint32_t)uniform((int)base);
+  const int32_t records = uniform(ok ? (int32_t)(kChunk * rb) : 0);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)ubase, (short)0, records, kBufferFlags);
+}
+
+// The chunk tile's 36 blocks of 1 KB are copied by: score wave i the rope
+// block of token octet i (block (i, 8)); value wave 4 + j the blocks
+// (r, 2j + h), r = 0..3, h = 0..1 -- the columns it multiplies itself.
+template <bool SCORE>
+constexpr int copy_loads() { return SCORE ? 1 : 8; }
+
+template <bool SCORE>
+__device__ __forceinline__ bool issue_copy(const DecodeArgs& a, const Chunk& c, uint32_t tile, int wave, int lane) {
+  if (!c.valid() || c.tok <= 0) return false;
+  const __amdgpu_buffer_rsrc_t rsrc = chunk_rsrc(a, c);
+  const uint32_t rb = (uint32_t)a.k_row_bytes;
   const int ta = lane >> 3, e = lane & 7;
-  if (wave < 4) {
-    const int t = 8 * wave + ta;
-    const uint32_t voff = t < tok ? t * rb + 16u * (64 + (e ^ ta ^ (2 * (wave & 1)))) : kOutOfRange;
-    lds_dma16(rsrc, voff, tile + 1024u * (9 * wave + 8));
-  } else {
-    const int j = wave - 4;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 8 * r + ta;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t voff = t < tok ? t * rb + 16u * (16 * j + 8 * h + (e ^ ta ^ (2 * (r & 1)))) : kOutOfRange;
-        lds_dma16(rsrc, voff, tile + 1024u * (9 * r + 2 * j + h));
-      }
-    }
+  for (int k = 0; k < copy_loads<SCORE>(); ++k) {
+    const int r = SCORE ? wave : (k >> 1);
+    const int q = SCORE ? 8 : 2 * (wave - 4) + (k & 1);
+    const int t = 8 * r + ta;
+    const uint32_t voff = t < c.tok ? t * rb + 16u * (8 * q + (e ^ ta ^ (2 * (r & 1)))) : kOutOfRange;
+    lds_dma16(rsrc, voff, tile + 1024u * (9 * r + q));
   }
   return true;
 }
 
 constexpr int kAheadK = 6;  // score k-steps whose K fragment is read ahead
+constexpr int kRingAhead = 5;  // chunks the bookkeeping runs ahead of the values
 
 // What a workgroup knows about its plan part.
 struct PartInfo {
@@ -239,12 +279,16 @@ struct PartInfo {
   int blk_row0;
 };
 
-// The decode loop of one role.  Both roles run the same cursor sequence and
-// meet the same workgroup barriers in the same order: every condition around a
-// barrier depends only on scalar bookkeeping shared by all waves or on flags
-// read from LDS after a barrier.  Each role has its own copy of the loop so
-// that the score state (queries) and the value state (accumulators) never
-// occupy registers at the same time.
+// The decode loop of one role.  Both roles step through the same chunk
+// descriptors and meet the same workgroup barriers in the same order (the
+// rare fix-up barrier sits after the score product in the score waves and
+// before the value product in the value waves): every condition around a
+// barrier depends only on the descriptors or on flags read from LDS after a
+// barrier.  Each role has its own copy of the loop so that the score state
+// (queries) and the value state (accumulators) never occupy registers at the
+// same time.  Within a step the score waves start their product at once and
+// the value waves first issue the copy, so each SIMD's matrix unit has work
+// while the other wave does its bookkeeping.
 template <int NRT, bool SCORE>
 __device__ __forceinline__ void decode_role(const DecodeArgs& a, const PartInfo& pi, lds_u8* const lds,
                                             const int wave, const int lane) {
@@ -253,7 +297,9 @@ __device__ __forceinline__ void decode_role(const DecodeArgs& a, const PartInfo&
   lds_f32* const cmax = (lds_f32*)(lds + kCmaxOffset);
   lds_i32* const flags = (lds_i32*)(lds + kFlagOffset);
   lds_f32* const fin = (lds_f32*)(lds + kFinalOffset);
+  lds_i32x4* const ring = (lds_i32x4*)(lds + kRingOffset);
   lds_u8* const plane = launder(lds + kPOffset + 16u * lane);
+  const bool producer = wave == 0;
 
   // ---- score role: rows 16 (rp0 + rt) + r16, token tile tt of each chunk
   const int tt = (wave & 3) >> 1;
@@ -286,12 +332,12 @@ __device__ __forceinline__ void decode_role(const DecodeArgs& a, const PartInfo&
   bool seg_bad = false;
   int seg_slot = 0, seg_nsplit = 1;
 
-  // Load the queries of the segment of chunk c and reset the score state.
-  // Waits for the loads here, before the next copy is issued, so that no later
-  // wait for them also waits for that copy.
-  auto begin_score_segment = [&](const Cursor& c) {
+  // Load the queries of the segment of chunk c and the visible-key limits of
+  // the score rows.  Waits for the loads here, before the next copy is issued,
+  // so that no later wait for them also waits for that copy.
+  auto load_queries = [&](const Chunk& c) {
     if constexpr (SCORE) {
-      const int n = clamp_len(a, c.n);
+      const int n = clamp_len(a, load_len(a, c.seq));
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
         const int row = pi.blk_row0 + 16 * (rp0 + rt) + r16;
@@ -305,49 +351,198 @@ __device__ __forceinline__ void decode_role(const DecodeArgs& a, const PartInfo&
           const bf16x8 v = *(const bf16x8*)(qp + 32 * ks);
           qf[rt][ks] = ok ? v : bf16x8{};
         }
-        m_own[rt] = -INFINITY;
-        lsum[rt] = 0.f;
-        lsumx[rt] = 0.f;
       }
       asm volatile("" ::"v"(qf[0][kKSteps - 1]), "v"(qf[1][kKSteps - 1]), "v"(qf[0][0]), "v"(qf[1][0]));
     }
   };
 
-  // ---- prologue: copies of chunks 0 and 1; queries of the first segment
-  Cursor S;  // chunk t + 1 (scores)
-  S.seq = pi.seq_begin;
-  S.chunk = 2 * pi.page_begin;
-  S.n = load_len(a, pi.seq_begin);
-  S.phys = load_phys(a, pi.seq_begin, pi.page_begin);
-  S.valid = true;
-  S.bad = false;
-  issue_copy(a, S, lds_addr, wave, lane);
-  Cursor L = next_chunk(a, S, pi.seq_last, pi.page_end);  // chunk t + 2 (landing)
-  issue_copy(a, L, lds_addr + kChunkBytes, wave, lane);
-  Cursor I = next_chunk(a, L, pi.seq_last, pi.page_end);  // chunk t + 3 (issued this step)
-  begin_score_segment(S);
+  // ---- prologue: wave 0 publishes chunks 0..3; copies of chunks 0 and 1;
+  // queries of the first segment
+  Cursor cur, nxt;  // producer: the next chunk to publish and the one after
+  bool prod_first = false;
+  if (producer) {
+    cur.seq = pi.seq_begin;
+    cur.chunk = 2 * pi.page_begin;
+    cur.n = load_len(a, pi.seq_begin);
+    cur.phys = load_phys(a, pi.seq_begin, pi.page_begin);
+    cur.valid = true;
+    prod_first = true;
+#pragma unroll 1
+    for (int k = 0; k < kRingAhead - 1; ++k) {
+      nxt = next_chunk(a, cur, pi.seq_last, pi.page_end);
+      const i32x4 d = pack_chunk(a, cur, nxt, prod_first);
+      if (lane == 0) ring[k] = d;
+      prod_first = !cur.valid || !nxt.valid || nxt.seq != cur.seq;
+      cur = nxt;
+    }
+    nxt = next_chunk(a, cur, pi.seq_last, pi.page_end);
+  }
+  block_sync();
+  Chunk D0 = unpack_chunk(i32x4{-1, 0, 0, -1});  // chunk t (values)
+  Chunk D1 = unpack_chunk(ring[0]);              // chunk t + 1 (scores)
+  Chunk D2 = unpack_chunk(ring[1]);              // chunk t + 2 (landing)
+  Chunk D3 = unpack_chunk(ring[2]);              // chunk t + 3 (copied this step)
+  issue_copy<SCORE>(a, D1, lds_addr, wave, lane);
+  issue_copy<SCORE>(a, D2, lds_addr + kChunkBytes, wave, lane);
+  if constexpr (SCORE) load_queries(D1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   block_sync();
-  Cursor V;  // chunk t (values)
-  V.valid = false;
-  V.seq = -1;
-  V.bad = false;
-  V.chunk = 0;
-  V.n = 0;
-  V.phys = -1;
-  int p_seq = -1;  // chunk t - 1: its sequence, -1 if none
-  bool p_valid = false;
+  bool p_last = false;  // chunk t - 1 ended its segment (the values still have to close it)
+  int p_seq = -1;
 
   for (int t = -1;; ++t) {
-    const bool v_has = V.valid && chunk_tokens(a, V) > 0;
-    const bool epi = p_valid && (!V.valid || V.seq != p_seq);
-    if (!V.valid && !S.valid && !epi) break;
-    const Cursor N = next_chunk(a, I, pi.seq_last, pi.page_end);  // chunk t + 4: fetch its length / entry now
+    if (!D0.valid() && !D1.valid() && !p_last) break;
     const int par = t & 1;
+    const bool v_has = D0.valid() && D0.tok > 0;
+    // LDS reads whose latency hides behind the first work of the step:
+    // chunk t's flags and the descriptor of chunk t + 4 (for the next step)
+    const i32x4 fl = *(const lds_i32x4*)(flags + 4 * par);
+    const i32x4 d4 = ring[(t + 4) & 7];
+    const uint32_t copy_tile = lds_addr + (uint32_t)((t + 3) & 3) * kChunkBytes;
+    bool issued = false;
 
-    if constexpr (!SCORE) {
+    if constexpr (SCORE) {
+      // ---- chunk t + 1 starts a segment: its queries (the first ones were
+      // loaded in the prologue)
+      if (D1.valid() && D1.first && t >= 0) load_queries(D1);
+      issued = issue_copy<SCORE>(a, D3, copy_tile, wave, lane);
+      // ---- scores of chunk t + 1: 32 rows x 16 tokens, two MFMAs per K read
+      const bool s_has = score_active && D1.valid() && D1.tok > 0;
+      f32x4 snew[2] = {};
+      if (s_has) {
+        lds_u8* const tile = lds + (uint32_t)((t + 1) & 3) * kChunkBytes;
+        lds_u8* const kb0 = launder(tile + k_lane + 16u * kx);
+        lds_u8* const kb1 = launder(tile + k_lane + 16u * (kx ^ 4u));
+        f32x4 acc[2][2] = {};  // [row tile][k-step parity]: independent MFMA chains
+        bf16x8 kf[kKSteps];
+#pragma unroll
+        for (int ks = 0; ks < kAheadK; ++ks) kf[ks] = *(const lds_bf16x8*)(((ks & 1) ? kb1 : kb0) + 1024u * (ks >> 1));
+#pragma unroll
+        for (int ks = 0; ks < kKSteps; ++ks) {
+          if (ks + kAheadK < kKSteps)
+            kf[ks + kAheadK] =
+                *(const lds_bf16x8*)((((ks + kAheadK) & 1) ? kb1 : kb0) + 1024u * ((ks + kAheadK) >> 1));
+          acc[0][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[0][ks], acc[0][ks & 1], 0, 0, 0);
+          acc[1][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[1][ks], acc[1][ks & 1], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        snew[0] = acc[0][0] + acc[0][1];
+        snew[1] = acc[1][0] + acc[1][1];
+      }
+      // ---- wave 0: publish chunk t + 5 (read from the ring from step t + 1 on)
+      if (producer) {
+        const i32x4 d = pack_chunk(a, cur, nxt, prod_first);
+        if (lane == 0) ring[(t + kRingAhead) & 7] = d;
+        prod_first = !cur.valid || !nxt.valid || nxt.seq != cur.seq;
+        cur = nxt;
+        nxt = next_chunk(a, cur, pi.seq_last, pi.page_end);
+      }
+      // ---- chunk t's flags: move the reference max where a chunk max passed it
+      if (v_has && uniform(fl[0] | fl[1] | fl[2] | fl[3])) {
+        if (score_active) {
+          const lds_f32* cm = cmax + par * 512 + r16;
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) {
+            const int rw = 16 * (rp0 + rt);
+            float m_new = m_own[rt];
+#pragma unroll
+            for (int gi = 0; gi < 8; ++gi) m_new = fmaxf(m_new, cm[64 * gi + rw]);
+            const float f = m_own[rt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_own[rt] - m_new);
+            lsum[rt] *= f;
+            lsumx[rt] *= f;
+            m_own[rt] = m_new;
+            const float mu = m_new == -INFINITY ? 0.f : m_new;
+            bf16x4 pv;
+            psum[rt] = 0.f;
+            psumx[rt] = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float e = __builtin_amdgcn_exp2f(sc[rt][j] - mu);
+              const __bf16 p = (__bf16)e;
+              psum[rt] += (float)p;
+              psumx[rt] += e;
+              pv[j] = p;
+            }
+            *(lds_bf16x4*)(plane + par * 4096 + 1024u * (rp0 + rt) + 8u * tt) = pv;
+          }
+        }
+        block_sync();  // ---- redone P visible (the value waves wait here before their product)
+      }
+      // ---- chunk t's probabilities are final: add their sums
+      if (v_has) {
+        lsum[0] += psum[0];
+        lsum[1] += psum[1];
+        lsumx[0] += psumx[0];
+        lsumx[1] += psumx[1];
+      }
+      // ---- chunk t ended its segment: publish the row totals
+      if (D0.valid() && D0.last && score_active) {
+        lds_f32* fs = fin + par * kFinalFloats;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          const float l = wave_sum16(lsum[rt]), lx = wave_sum16(lsumx[rt]);
+          const int rw = 16 * (rp0 + rt) + r16;
+          if (g == 0) {
+            fs[kFinalSum + 64 * tt + rw] = l;
+            fs[kFinalSumX + 64 * tt + rw] = lx;
+            if (tt == 0) fs[kFinalRef + rw] = m_own[rt];
+          }
+        }
+      }
+      // ---- chunk t + 1 starts a segment: fresh softmax state
+      if (D1.valid() && D1.first) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          m_own[rt] = -INFINITY;
+          lsum[rt] = 0.f;
+          lsumx[rt] = 0.f;
+        }
+      }
+      if (s_has) {
+        // ---- mask, scale, optimistic probabilities of chunk t + 1;
+        // token 32 chunk + 16 tt + 4 g + j
+        sc[0] = snew[0];
+        sc[1] = snew[1];
+        const int base_tok = kChunk * D1.chunk + 16 * tt + 4 * g;
+        const int par1 = (t + 1) & 1;
+        bool over = false;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          const int vis = lim[rt] - base_tok;
+          float mx = -INFINITY;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float x = j < vis ? sc[rt][j] * a.scale_log2 : -INFINITY;
+            sc[rt][j] = x;
+            mx = fmaxf(mx, x);
+          }
+          over |= mx > m_own[rt] + kRescaleSlack;
+          cmax[par1 * 512 + 64 * (4 * tt + g) + 16 * (rp0 + rt) + r16] = mx;
+          const float mu = m_own[rt] == -INFINITY ? 0.f : m_own[rt];
+          bf16x4 pv;
+          psum[rt] = 0.f;
+          psumx[rt] = 0.f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float e = __builtin_amdgcn_exp2f(sc[rt][j] - mu);
+            const __bf16 p = (__bf16)e;
+            psum[rt] += (float)p;
+            psumx[rt] += e;
+            pv[j] = p;
+          }
+          *(lds_bf16x4*)(plane + par1 * 4096 + 1024u * (rp0 + rt) + 8u * tt) = pv;
+        }
+        const bool wave_over = __builtin_amdgcn_ballot_w64(over) != 0;
+        if (lane == 0) flags[4 * par1 + wave] = wave_over ? 1 : 0;
+      } else if (lane == 0) {
+        flags[4 * ((t + 1) & 1) + wave] = 0;
+      }
+    } else {
+      // ---- copy chunk t + 3 into the tile chunk t - 1 used, first thing in
+      // the step -- unless a segment closes here, whose stores go first
+      if (!p_last) issued = issue_copy<SCORE>(a, D3, copy_tile, wave, lane);
       // ---- close the segment that ended with chunk t - 1
-      if (epi) {
+      if (p_last) {
         const lds_f32* fs = fin + ((t - 1) & 1) * kFinalFloats + r16;
         const bool final_out = seg_nsplit == 1;
         int row0 = pi.blk_row0 + r16;  // opaque: keeps the address arithmetic in this block
@@ -386,150 +581,32 @@ __device__ __forceinline__ void decode_role(const DecodeArgs& a, const PartInfo&
           for (int ct = 0; ct < 8; ++ct) o[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
           mref[rt] = -INFINITY;
         }
+        issued = issue_copy<SCORE>(a, D3, copy_tile, wave, lane);
       }
-      if (V.valid && (!p_valid || V.seq != p_seq)) {  // the values enter a new segment
-        const int split = V.seq == pi.seq_begin ? pi.split_first : 0;
-        const int s0 = ((cint32*)a.num_splits)[V.seq];
+      if (D0.valid() && D0.first) {  // the values enter a new segment
+        const int split = D0.seq == pi.seq_begin ? pi.split_first : 0;
+        const int s0 = ((cint32*)a.num_splits)[D0.seq];
         seg_slot = s0 + split;
-        seg_nsplit = ((cint32*)a.num_splits)[V.seq + 1] - s0;
+        seg_nsplit = ((cint32*)a.num_splits)[D0.seq + 1] - s0;
         seg_bad = false;
       }
-    }
-
-    // ---- chunk t's flags: move the reference max where a chunk max passed it
-    if (v_has) {
-      const i32x4 fl = *(const lds_i32x4*)(flags + 4 * par);
-      if (uniform(fl[0] | fl[1] | fl[2] | fl[3])) {
+      if (D0.valid()) seg_bad |= D0.bad;
+      // ---- chunk t's flags: rescale what the rows whose reference moved
+      // have accumulated, then wait for the redone P
+      if (v_has && uniform(fl[0] | fl[1] | fl[2] | fl[3])) {
         const lds_f32* cm = cmax + par * 512 + r16;
-        if constexpr (SCORE) {
-          if (score_active) {
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-              const int rw = 16 * (rp0 + rt);
-              float m_new = m_own[rt];
+        for (int rt = 0; rt < NRT; ++rt) {
+          float m_new = mref[rt];
 #pragma unroll
-              for (int gi = 0; gi < 8; ++gi) m_new = fmaxf(m_new, cm[64 * gi + rw]);
-              const float f = m_own[rt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_own[rt] - m_new);
-              lsum[rt] *= f;
-              lsumx[rt] *= f;
-              m_own[rt] = m_new;
-              const float mu = m_new == -INFINITY ? 0.f : m_new;
-              bf16x4 pv;
-              psum[rt] = 0.f;
-              psumx[rt] = 0.f;
+          for (int gi = 0; gi < 8; ++gi) m_new = fmaxf(m_new, cm[64 * gi + 16 * rt]);
+          const float f = mref[rt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mref[rt] - m_new);
+          mref[rt] = m_new;
 #pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const float e = __builtin_amdgcn_exp2f(sc[rt][j] - mu);
-                const __bf16 p = (__bf16)e;
-                psum[rt] += (float)p;
-                psumx[rt] += e;
-                pv[j] = p;
-              }
-              *(lds_bf16x4*)(plane + par * 4096 + 1024u * (rp0 + rt) + 8u * tt) = pv;
-            }
-          }
-        } else {
-#pragma unroll
-          for (int rt = 0; rt < NRT; ++rt) {
-            float m_new = mref[rt];
-#pragma unroll
-            for (int gi = 0; gi < 8; ++gi) m_new = fmaxf(m_new, cm[64 * gi + 16 * rt]);
-            const float f = mref[rt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mref[rt] - m_new);
-            mref[rt] = m_new;
-#pragma unroll
-            for (int ct = 0; ct < 8; ++ct) o[rt][ct] *= f;
-          }
+          for (int ct = 0; ct < 8; ++ct) o[rt][ct] *= f;
         }
         block_sync();  // ---- redone P visible
       }
-    }
-
-    if constexpr (SCORE) {
-      // ---- chunk t's probabilities are final: add their sums
-      if (v_has) {
-        lsum[0] += psum[0];
-        lsum[1] += psum[1];
-        lsumx[0] += psumx[0];
-        lsumx[1] += psumx[1];
-      }
-      // ---- chunk t ended its segment: publish the row totals
-      if (V.valid && (!S.valid || S.seq != V.seq) && score_active) {
-        lds_f32* fs = fin + par * kFinalFloats;
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-          const float l = wave_sum16(lsum[rt]), lx = wave_sum16(lsumx[rt]);
-          const int rw = 16 * (rp0 + rt) + r16;
-          if (g == 0) {
-            fs[kFinalSum + 64 * tt + rw] = l;
-            fs[kFinalSumX + 64 * tt + rw] = lx;
-            if (tt == 0) fs[kFinalRef + rw] = m_own[rt];
-          }
-        }
-      }
-      // ---- chunk t + 1 starts a segment: its queries
-      if (S.valid && V.valid && S.seq != V.seq) begin_score_segment(S);
-    }
-
-    // ---- copy chunk t + 3 into the tile chunk t - 1 used
-    const bool issued = issue_copy(a, I, lds_addr + (uint32_t)((t + 3) & 3) * kChunkBytes, wave, lane);
-
-    if constexpr (SCORE) {
-      if (score_active && S.valid && chunk_tokens(a, S) > 0) {
-        // ---- scores of chunk t + 1: 32 rows x 16 tokens, two MFMAs per K read
-        lds_u8* const tile = lds + (uint32_t)((t + 1) & 3) * kChunkBytes;
-        lds_u8* const kb0 = launder(tile + k_lane + 16u * kx);
-        lds_u8* const kb1 = launder(tile + k_lane + 16u * (kx ^ 4u));
-        sc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-        sc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        bf16x8 kf[kKSteps];
-#pragma unroll
-        for (int ks = 0; ks < kAheadK; ++ks) kf[ks] = *(const lds_bf16x8*)(((ks & 1) ? kb1 : kb0) + 1024u * (ks >> 1));
-#pragma unroll
-        for (int ks = 0; ks < kKSteps; ++ks) {
-          if (ks + kAheadK < kKSteps)
-            kf[ks + kAheadK] =
-                *(const lds_bf16x8*)((((ks + kAheadK) & 1) ? kb1 : kb0) + 1024u * ((ks + kAheadK) >> 1));
-          sc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[0][ks], sc[0], 0, 0, 0);
-          sc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[1][ks], sc[1], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        // ---- mask, scale; token 32 chunk + 16 tt + 4 g + j
-        const int base_tok = kChunk * S.chunk + 16 * tt + 4 * g;
-        const int par1 = (t + 1) & 1;
-        bool over = false;
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-          const int vis = lim[rt] - base_tok;
-          float mx = -INFINITY;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float x = j < vis ? sc[rt][j] * a.scale_log2 : -INFINITY;
-            sc[rt][j] = x;
-            mx = fmaxf(mx, x);
-          }
-          over |= mx > m_own[rt] + kRescaleSlack;
-          cmax[par1 * 512 + 64 * (4 * tt + g) + 16 * (rp0 + rt) + r16] = mx;
-          const float mu = m_own[rt] == -INFINITY ? 0.f : m_own[rt];
-          bf16x4 pv;
-          psum[rt] = 0.f;
-          psumx[rt] = 0.f;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float e = __builtin_amdgcn_exp2f(sc[rt][j] - mu);
-            const __bf16 p = (__bf16)e;
-            psum[rt] += (float)p;
-            psumx[rt] += e;
-            pv[j] = p;
-          }
-          *(lds_bf16x4*)(plane + par1 * 4096 + 1024u * (rp0 + rt) + 8u * tt) = pv;
-        }
-        const bool wave_over = __builtin_amdgcn_ballot_w64(over) != 0;
-        if (lane == 0) flags[4 * par1 + wave] = wave_over ? 1 : 0;
-      } else if (lane == 0) {
-        flags[4 * ((t + 1) & 1) + wave] = 0;
-      }
-    } else {
-      if (V.valid) seg_bad |= V.bad;
       if (v_has) {
         // ---- O^T[columns 128 vj ..] += V^T . P^T for chunk t
         lds_u8* const tile = lds + (uint32_t)(t & 3) * kChunkBytes;
@@ -550,11 +627,13 @@ __device__ __forceinline__ void decode_role(const DecodeArgs& a, const PartInfo&
             o[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rt], o[rt][ct], 0, 0, 0);
         }
       }
+      p_seq = D0.seq;
     }
 
     // ---- end of step: this wave's share of chunk t + 2 has landed and all
     // LDS reads of the step have returned
     if (issued) {
+      static_assert(copy_loads<true>() == 1 && copy_loads<false>() == 8, "vmcnt below");
       if constexpr (SCORE)
         asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
       else
@@ -563,12 +642,11 @@ __device__ __forceinline__ void decode_role(const DecodeArgs& a, const PartInfo&
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     block_sync();
-    p_seq = V.seq;
-    p_valid = V.valid;
-    V = S;
-    S = L;
-    L = I;
-    I = N;
+    p_last = D0.valid() && D0.last;
+    D0 = D1;
+    D1 = D2;
+    D2 = D3;
+    D3 = unpack_chunk(d4);
   }
 }
 
