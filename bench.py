@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+from paged_mla_decode_04_amd import traffic
 from paged_mla_decode_04_amd import (_lib, default_num_parts, get_mla_metadata,  # noqa: E402
                                      mla_decode_with_kvcache, workspace_size)
 from paged_mla_decode_04_amd import metrics  # noqa: E402
@@ -202,6 +203,11 @@ def main():
             "traffic": None,
         },
     }
+    # measured HBM bytes per decode call (FETCH_SIZE + WRITE_SIZE, copy-calibrated),
+    # only when the counters were taken on the current kernel sources
+    tr = traffic.load(w.name)
+    if tr is not None:
+        line["roofline"]["traffic"] = round(tr["bytes_per_call"])
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp_host, args.cpu_seconds)
     print(json.dumps(line), flush=True)
