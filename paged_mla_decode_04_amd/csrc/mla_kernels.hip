@@ -191,8 +191,8 @@ __device__ __forceinline__ Cursor next_chunk(const DecodeArgs& a, const Cursor& 
   return d;
 }
 
-// What every wave needs to know about one chunk.  Wave 0 walks the part with a
-// Cursor and publishes these, five chunks ahead, in a ring of eight LDS slots
+// What every wave needs to know about one chunk.  Wave 4 walks the part with a
+// Cursor and publishes these, six chunks ahead, in a ring of eight LDS slots
 // (16 bytes each), so that the page bookkeeping costs the CU's scalar unit one
 // wave's work instead of eight.
 struct Chunk {
@@ -271,7 +271,7 @@ __device__ __forceinline__ bool issue_copy(const DecodeArgs& a, const Chunk& c, 
 }
 
 constexpr int kAheadK = 6;  // score k-steps whose K fragment is read ahead
-constexpr int kRingAhead = 5;  // chunks the bookkeeping runs ahead of the values
+constexpr int kRingAhead = 6;  // chunks the bookkeeping runs ahead of the values
 
 // What a workgroup knows about its plan part.
 struct PartInfo {
@@ -299,7 +299,7 @@ __device__ __forceinline__ void decode_role(const DecodeArgs& a, const PartInfo&
   lds_f32* const fin = (lds_f32*)(lds + kFinalOffset);
   lds_i32x4* const ring = (lds_i32x4*)(lds + kRingOffset);
   lds_u8* const plane = launder(lds + kPOffset + 16u * lane);
-  const bool producer = wave == 0;
+  const bool producer = wave == 4;  // a value wave: they wait for the score waves at every barrier
 
   // ---- score role: rows 16 (rp0 + rt) + r16, token tile tt of each chunk
   const int tt = (wave & 3) >> 1;
@@ -356,7 +356,7 @@ __device__ __forceinline__ void decode_role(const DecodeArgs& a, const PartInfo&
     }
   };
 
-  // ---- prologue: wave 0 publishes chunks 0..3; copies of chunks 0 and 1;
+  // ---- prologue: wave 4 publishes chunks 0..4; copies of chunks 0, 1 and 2;
   // queries of the first segment
   Cursor cur, nxt;  // producer: the next chunk to publish and the one after
   bool prod_first = false;
@@ -381,31 +381,41 @@ __device__ __forceinline__ void decode_role(const DecodeArgs& a, const PartInfo&
   Chunk D0 = unpack_chunk(i32x4{-1, 0, 0, -1});  // chunk t (values)
   Chunk D1 = unpack_chunk(ring[0]);              // chunk t + 1 (scores)
   Chunk D2 = unpack_chunk(ring[1]);              // chunk t + 2 (landing)
-  Chunk D3 = unpack_chunk(ring[2]);              // chunk t + 3 (copied this step)
+  Chunk D3 = unpack_chunk(ring[2]);              // chunk t + 3 (in flight)
+  Chunk D4 = unpack_chunk(ring[3]);              // chunk t + 4 (copied this step)
   issue_copy<SCORE>(a, D1, lds_addr, wave, lane);
   issue_copy<SCORE>(a, D2, lds_addr + kChunkBytes, wave, lane);
+  issue_copy<SCORE>(a, D3, lds_addr + 2 * kChunkBytes, wave, lane);
   if constexpr (SCORE) load_queries(D1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   block_sync();
   bool p_last = false;  // chunk t - 1 ended its segment (the values still have to close it)
   int p_seq = -1;
+  bool iss_prev = false;  // this wave issued loads for chunk t + 3 (in the previous step)
+  // value role: V^T operands of chunk t (read from its tile one step early, so
+  // the tile is free for the next copy as soon as the scores are done with it)
+  bf16x8 vcur[SCORE ? 1 : 8], vnext[SCORE ? 1 : 8];
 
   for (int t = -1;; ++t) {
     if (!D0.valid() && !D1.valid() && !p_last) break;
     const int par = t & 1;
     const bool v_has = D0.valid() && D0.tok > 0;
     // LDS reads whose latency hides behind the first work of the step:
-    // chunk t's flags and the descriptor of chunk t + 4 (for the next step)
+    // chunk t's flags and the descriptor of chunk t + 5 (for the next step)
     const i32x4 fl = *(const lds_i32x4*)(flags + 4 * par);
-    const i32x4 d4 = ring[(t + 4) & 7];
-    const uint32_t copy_tile = lds_addr + (uint32_t)((t + 3) & 3) * kChunkBytes;
+    const i32x4 d5 = ring[(t + 5) & 7];
+    // chunk t + 4 goes into the tile of chunk t, whose last reader (step t - 1) is done
+    const uint32_t copy_tile = lds_addr + (uint32_t)((t + 4) & 3) * kChunkBytes;
     bool issued = false;
 
     if constexpr (SCORE) {
       // ---- chunk t + 1 starts a segment: its queries (the first ones were
       // loaded in the prologue)
       if (D1.valid() && D1.first && t >= 0) load_queries(D1);
-      issued = issue_copy<SCORE>(a, D3, copy_tile, wave, lane);
+      issued = issue_copy<SCORE>(a, D4, copy_tile, wave, lane);
+      // the score chain (product, softmax, P) is the step's critical path: let
+      // its instructions go first on the SIMD the value wave shares
+      __builtin_amdgcn_s_setprio(1);
       // ---- scores of chunk t + 1: 32 rows x 16 tokens, two MFMAs per K read
       const bool s_has = score_active && D1.valid() && D1.tok > 0;
       f32x4 snew[2] = {};
@@ -429,14 +439,6 @@ __device__ __forceinline__ void decode_role(const DecodeArgs& a, const PartInfo&
         snew[0] = acc[0][0] + acc[0][1];
         snew[1] = acc[1][0] + acc[1][1];
       }
-      // ---- wave 0: publish chunk t + 5 (read from the ring from step t + 1 on)
-      if (producer) {
-        const i32x4 d = pack_chunk(a, cur, nxt, prod_first);
-        if (lane == 0) ring[(t + kRingAhead) & 7] = d;
-        prod_first = !cur.valid || !nxt.valid || nxt.seq != cur.seq;
-        cur = nxt;
-        nxt = next_chunk(a, cur, pi.seq_last, pi.page_end);
-      }
       // ---- chunk t's flags: move the reference max where a chunk max passed it
       if (v_has && uniform(fl[0] | fl[1] | fl[2] | fl[3])) {
         if (score_active) {
@@ -446,7 +448,8 @@ __device__ __forceinline__ void decode_role(const DecodeArgs& a, const PartInfo&
             const int rw = 16 * (rp0 + rt);
             float m_new = m_own[rt];
 #pragma unroll
-            for (int gi = 0; gi < 8; ++gi) m_new = fmaxf(m_new, cm[64 * gi + rw]);
+            for (int gi = 0; gi < 8; ++gi)  // group gi = 4 * token tile + lane group, written by wave 2 tt + (row tile / 2)
+              if (uniform(fl[2 * (gi >> 2) + (rp0 >> 1)])) m_new = fmaxf(m_new, cm[64 * gi + rw]);
             const float f = m_own[rt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_own[rt] - m_new);
             lsum[rt] *= f;
             lsumx[rt] *= f;
@@ -506,6 +509,7 @@ __device__ __forceinline__ void decode_role(const DecodeArgs& a, const PartInfo&
         const int base_tok = kChunk * D1.chunk + 16 * tt + 4 * g;
         const int par1 = (t + 1) & 1;
         bool over = false;
+        float cmx[2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
           const int vis = lim[rt] - base_tok;
@@ -517,7 +521,7 @@ __device__ __forceinline__ void decode_role(const DecodeArgs& a, const PartInfo&
             mx = fmaxf(mx, x);
           }
           over |= mx > m_own[rt] + kRescaleSlack;
-          cmax[par1 * 512 + 64 * (4 * tt + g) + 16 * (rp0 + rt) + r16] = mx;
+          cmx[rt] = mx;
           const float mu = m_own[rt] == -INFINITY ? 0.f : m_own[rt];
           bf16x4 pv;
           psum[rt] = 0.f;
@@ -533,14 +537,21 @@ __device__ __forceinline__ void decode_role(const DecodeArgs& a, const PartInfo&
           *(lds_bf16x4*)(plane + par1 * 4096 + 1024u * (rp0 + rt) + 8u * tt) = pv;
         }
         const bool wave_over = __builtin_amdgcn_ballot_w64(over) != 0;
+        // the chunk maxima are only read when some wave is flagged, and then
+        // only those of the flagged waves
+        if (wave_over) {
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) cmax[par1 * 512 + 64 * (4 * tt + g) + 16 * (rp0 + rt) + r16] = cmx[rt];
+        }
         if (lane == 0) flags[4 * par1 + wave] = wave_over ? 1 : 0;
       } else if (lane == 0) {
         flags[4 * ((t + 1) & 1) + wave] = 0;
       }
+      __builtin_amdgcn_s_setprio(0);
     } else {
-      // ---- copy chunk t + 3 into the tile chunk t - 1 used, first thing in
-      // the step -- unless a segment closes here, whose stores go first
-      if (!p_last) issued = issue_copy<SCORE>(a, D3, copy_tile, wave, lane);
+      // ---- copy chunk t + 4, first thing in the step -- unless a segment
+      // closes here, whose stores go first
+      if (!p_last) issued = issue_copy<SCORE>(a, D4, copy_tile, wave, lane);
       // ---- close the segment that ended with chunk t - 1
       if (p_last) {
         const lds_f32* fs = fin + ((t - 1) & 1) * kFinalFloats + r16;
@@ -581,7 +592,7 @@ __device__ __forceinline__ void decode_role(const DecodeArgs& a, const PartInfo&
           for (int ct = 0; ct < 8; ++ct) o[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
           mref[rt] = -INFINITY;
         }
-        issued = issue_copy<SCORE>(a, D3, copy_tile, wave, lane);
+        issued = issue_copy<SCORE>(a, D4, copy_tile, wave, lane);
       }
       if (D0.valid() && D0.first) {  // the values enter a new segment
         const int split = D0.seq == pi.seq_begin ? pi.split_first : 0;
@@ -591,6 +602,14 @@ __device__ __forceinline__ void decode_role(const DecodeArgs& a, const PartInfo&
         seg_bad = false;
       }
       if (D0.valid()) seg_bad |= D0.bad;
+      // ---- wave 4: publish chunk t + 5 (read from the ring from step t + 1 on)
+      if (producer) {
+        const i32x4 d = pack_chunk(a, cur, nxt, prod_first);
+        if (lane == 0) ring[(t + kRingAhead) & 7] = d;
+        prod_first = !cur.valid || !nxt.valid || nxt.seq != cur.seq;
+        cur = nxt;
+        nxt = next_chunk(a, cur, pi.seq_last, pi.page_end);
+      }
       // ---- chunk t's flags: rescale what the rows whose reference moved
       // have accumulated, then wait for the redone P
       if (v_has && uniform(fl[0] | fl[1] | fl[2] | fl[3])) {
@@ -599,7 +618,8 @@ __device__ __forceinline__ void decode_role(const DecodeArgs& a, const PartInfo&
         for (int rt = 0; rt < NRT; ++rt) {
           float m_new = mref[rt];
 #pragma unroll
-          for (int gi = 0; gi < 8; ++gi) m_new = fmaxf(m_new, cm[64 * gi + 16 * rt]);
+          for (int gi = 0; gi < 8; ++gi)
+            if (uniform(fl[2 * (gi >> 2) + (rt >> 1)])) m_new = fmaxf(m_new, cm[64 * gi + 16 * rt]);
           const float f = mref[rt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mref[rt] - m_new);
           mref[rt] = m_new;
 #pragma unroll
@@ -607,33 +627,47 @@ __device__ __forceinline__ void decode_role(const DecodeArgs& a, const PartInfo&
         }
         block_sync();  // ---- redone P visible
       }
-      if (v_has) {
-        // ---- O^T[columns 128 vj ..] += V^T . P^T for chunk t
-        lds_u8* const tile = lds + (uint32_t)(t & 3) * kChunkBytes;
+      // ---- V^T operands of chunk t + 1 from its tile (the scores read it now too)
+      if (D1.valid() && D1.tok > 0) {
+        lds_u8* const tile = lds + (uint32_t)((t + 1) & 3) * kChunkBytes;
         lds_u8* vb[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) vb[u] = launder(tile + v_lane + 16u * ((2u * u) ^ vy));
-        bf16x8 pf[NRT];
-#pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) pf[rt] = *(const lds_bf16x8*)(plane + par * 4096 + 1024u * rt);
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) {
           const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb[ct & 3] + 1024u * (ct >> 2)));
           const bf16x4 hi =
               __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb[ct & 3] + 1024u * (ct >> 2) + 18432u));
-          const bf16x8 vf = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-          for (int rt = 0; rt < NRT; ++rt)
-            o[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rt], o[rt][ct], 0, 0, 0);
+          vnext[ct] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
       }
+      if (v_has) {
+        // ---- O^T[columns 128 vj ..] += V^T . P^T for chunk t
+        bf16x8 pf[NRT];
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) pf[rt] = *(const lds_bf16x8*)(plane + par * 4096 + 1024u * rt);
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+          for (int rt = 0; rt < NRT; ++rt)
+            o[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vcur[ct], pf[rt], o[rt][ct], 0, 0, 0);
+      }
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) vcur[ct] = vnext[ct];
       p_seq = D0.seq;
     }
 
-    // ---- end of step: this wave's share of chunk t + 2 has landed and all
-    // LDS reads of the step have returned
-    if (issued) {
-      static_assert(copy_loads<true>() == 1 && copy_loads<false>() == 8, "vmcnt below");
+    // ---- end of step: this wave's share of chunk t + 2 has landed (the copies
+    // of chunks t + 3 and t + 4, issued after it, may still be in flight) and
+    // all LDS reads of the step have returned
+    static_assert(copy_loads<true>() == 1 && copy_loads<false>() == 8, "vmcnt below");
+    const int pending = (iss_prev ? 1 : 0) + (issued ? 1 : 0);
+    if (pending == 2) {
+      if constexpr (SCORE)
+        asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    } else if (pending == 1) {
       if constexpr (SCORE)
         asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
       else
@@ -642,11 +676,13 @@ __device__ __forceinline__ void decode_role(const DecodeArgs& a, const PartInfo&
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     block_sync();
+    iss_prev = issued;
     p_last = D0.valid() && D0.last;
     D0 = D1;
     D1 = D2;
     D2 = D3;
-    D3 = unpack_chunk(d4);
+    D3 = D4;
+    D4 = unpack_chunk(d5);
   }
 }
 
