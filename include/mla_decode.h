@@ -67,7 +67,7 @@ typedef enum mla_status {
 /* int32 values per part in the tile-scheduler metadata. */
 #define MLA_TILE_MD_INTS 8
 /* Rows (s_q * h_q / h_kv) handled by one workgroup; more rows use several. */
-#define MLA_ROWS_PER_WORKGROUP 64
+#define MLA_ROWS_PER_WORKGROUP 128
 /* Upper bound on s_q * h_q / h_kv. */
 #define MLA_MAX_ROWS 1024
 

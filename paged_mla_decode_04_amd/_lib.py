@@ -22,7 +22,7 @@ MLA_ERR_WORKSPACE_TOO_SMALL = 5
 MLA_ERR_HIP = 6
 MLA_ERR_BAD_ARGUMENT = 7
 TILE_MD_INTS = 8
-ROWS_PER_WORKGROUP = 64
+ROWS_PER_WORKGROUP = 128
 MAX_ROWS = 1024
 
 EXPORTS = (

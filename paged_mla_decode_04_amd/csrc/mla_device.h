@@ -1,0 +1,196 @@
+// Device helpers shared by the decode kernels: operand types, the chunk
+// descriptors of the page walk and the LDS-direct copy.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla_internal.h"
+#include "mla_plan.h"
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) int32_t lds_i32;
+
+constexpr int kD = 576;
+constexpr int kDv = 512;
+constexpr int kPageBytes = 64 * kD * 2;  // 73728
+constexpr int kKSteps = kD / 32;          // 18 MFMA k-steps of 32 for the scores
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleSlack = 16.0f;    // log2 units: p = 2^(x - m) stays <= 65536
+constexpr int32_t kBufferFlags = 0x00020000;
+constexpr uint32_t kOutOfRange = 0x7FFFF000u;
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ float wave_max16(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float wave_sum16(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// Opaque copy of an LDS pointer: keeps base + constant address arithmetic from
+// being re-associated (and hoisted) so the constant lands in the instruction
+// offset field.
+__device__ __forceinline__ lds_u8* launder(lds_u8* p) {
+  asm volatile("" : "+v"(p));
+  return p;
+}
+
+// Workgroup barrier for LDS hand-offs.  The page copies are waited for
+// explicitly (vmcnt) before it; unlike __syncthreads it does not also wait for
+// the next page's copies still in flight.
+__device__ __forceinline__ void block_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+constexpr int kChunk = 32;  // tokens per pipeline step (half a page)
+
+typedef const __attribute__((address_space(4))) int32_t cint32;  // read-only, uniform: scalar loads
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
+
+// 16-byte LDS-direct buffer load: lane l's 16 bytes land at lds_addr + 16 l.
+// Written as inline assembly so that the compiler does not track the LDS
+// write: it would otherwise make every later LDS read wait for all copies in
+// flight.  Completion is awaited explicitly (vmcnt) before the barrier that
+// hands a chunk over, and a copy only targets a tile no wave reads any more.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr) : "memory");
+}
+// Position of the page-bookkeeping cursor: one 32-token chunk of the part's
+// (sequence, chunk) order.
+struct Cursor {
+  int seq, chunk;  // sequence, chunk within the sequence (page chunk / 2)
+  int n;           // cached tokens of seq as stored (clamp_len applies the cap)
+  int phys;        // block-table entry of the chunk's page (-1 past the row)
+  bool valid;      // inside the part
+};
+
+__device__ __forceinline__ int clamp_len(const DecodeArgs& a, int n) {
+  const int cap = a.max_blocks * kPageTokens;
+  return n < 0 ? 0 : (n > cap ? cap : n);
+}
+__device__ __forceinline__ int load_len(const DecodeArgs& a, int b) { return ((cint32*)a.seqlens)[b]; }
+__device__ __forceinline__ int load_phys(const DecodeArgs& a, int b, int page) {
+  return page < a.max_blocks ? ((cint32*)a.block_table)[(int64_t)b * a.bt_stride + page] : -1;
+}
+// chunks a sequence of n tokens occupies; an empty sequence owns one empty chunk
+__device__ __forceinline__ int chunk_count(int n) { return n <= 0 ? 1 : (n + kChunk - 1) / kChunk; }
+
+// The chunk after c in the part.  Uses c.n, fetched at least a step earlier;
+// starts the fetch of a new sequence's length and of a new page's table entry.
+__device__ __forceinline__ Cursor next_chunk(const DecodeArgs& a, const Cursor& c, int seq_last, int page_end) {
+  Cursor d = c;
+  if (!c.valid) return d;
+  int end = chunk_count(clamp_len(a, c.n));
+  if (c.seq == seq_last && 2 * page_end < end) end = 2 * page_end;
+  if (c.chunk + 1 < end) {
+    d.chunk = c.chunk + 1;
+    if ((d.chunk & 1) == 0) d.phys = load_phys(a, d.seq, d.chunk >> 1);
+  } else if (c.seq < seq_last) {
+    d.seq = c.seq + 1;
+    d.chunk = 0;
+    d.n = load_len(a, d.seq);
+    d.phys = load_phys(a, d.seq, 0);
+  } else {
+    d.valid = false;
+  }
+  return d;
+}
+
+// What every wave needs to know about one chunk.  Wave 4 walks the part with a
+// Cursor and publishes these, six chunks ahead, in a ring of eight LDS slots
+// (16 bytes each), so that the page bookkeeping costs the CU's scalar unit one
+// wave's work instead of eight.
+struct Chunk {
+  int seq;     // -1: past the end of the part
+  int chunk;   // within the sequence
+  int tok;     // tokens in the chunk (0 for an empty sequence's chunk)
+  int phys;    // block-table entry of its page
+  bool first;  // first chunk of its segment (the part's piece of one sequence)
+  bool last;   // last chunk of its segment
+  bool bad;    // the entry lies outside the pool
+  __device__ bool valid() const { return seq >= 0; }
+};
+
+__device__ __forceinline__ i32x4 pack_chunk(const DecodeArgs& a, const Cursor& c, const Cursor& next, bool first) {
+  i32x4 d;
+  if (!c.valid) {
+    d = i32x4{-1, 0, 0, -1};
+    return d;
+  }
+  int tok = clamp_len(a, c.n) - kChunk * c.chunk;
+  tok = tok < 0 ? 0 : (tok > kChunk ? kChunk : tok);
+  const bool last = !next.valid || next.seq != c.seq;
+  const bool bad = tok > 0 && !(c.phys >= 0 && c.phys < a.num_blocks);
+  d = i32x4{c.seq, c.chunk, tok | (first ? 256 : 0) | (last ? 512 : 0) | (bad ? 1024 : 0), c.phys};
+  return d;
+}
+
+__device__ __forceinline__ Chunk unpack_chunk(const i32x4 d) {
+  Chunk c;
+  c.seq = uniform(d[0]);
+  c.chunk = uniform(d[1]);
+  const int z = uniform(d[2]);
+  c.phys = uniform(d[3]);
+  c.tok = z & 255;
+  c.first = (z & 256) != 0;
+  c.last = (z & 512) != 0;
+  c.bad = (z & 1024) != 0;
+  return c;
+}
+
+// Source of one chunk's copy: a buffer resource over the chunk's valid rows
+// (zero records for a page outside the pool, so it reads as zeros): rows at or
+// past the chunk's token count read as zeros through the range check.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const DecodeArgs& a, const Chunk& c) {
+  const bool ok = !c.bad;
+  const uint32_t rb = (uint32_t)a.k_row_bytes;
+  const uint64_t base =
+      (uint64_t)(a.k + (ok ? (int64_t)c.phys * a.k_block_bytes + (int64_t)(c.chunk & 1) * kChunk * rb : 0));
+  // the descriptor fields are wave-uniform; say so, so the resource lands in scalar registers
+  const uint64_t ubase = ((uint64_t)(uint32_t)uniform((int)(base >> 32)) << 32) | (uint32_t)uniform((int)base);
+  const int32_t records = uniform(ok ? (int32_t)(c.tok * rb) : 0);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)ubase, (short)0, records, kBufferFlags);
+}
+
+// What a workgroup knows about its plan part.
+struct PartInfo {
+  int seq_begin, page_begin, seq_last, page_end, split_first;
+  int blk_row0;
+};
+
+// Workgroups are dealt round-robin to the 8 XCDs; give each XCD a contiguous
+// run of (part, row block) pairs so that the row blocks of one part, and
+// neighbouring parts of one sequence, share that XCD's L2.  Returns false
+// for an idle part.
+__device__ __forceinline__ bool load_part(const DecodeArgs& a, int rows_per_block, PartInfo& pi) {
+  const int G = gridDim.x, hw = blockIdx.x;
+  const int xcd = hw & 7, pos = hw >> 3;
+  const int logical = xcd * (G >> 3) + min(xcd, G & 7) + pos;
+  const int part = logical / a.row_blocks;
+  const int mblock = logical - part * a.row_blocks;
+  cint32* md = (cint32*)a.tile_md + (int64_t)part * kTileMdInts;
+  pi.seq_begin = md[0];
+  if (pi.seq_begin >= a.batch) return false;
+  pi.page_begin = md[1];
+  pi.seq_last = md[2];
+  pi.page_end = md[3];
+  pi.split_first = md[4];
+  pi.blk_row0 = mblock * rows_per_block;
+  return true;
+}
+
+}  // namespace mla

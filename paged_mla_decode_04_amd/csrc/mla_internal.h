@@ -31,6 +31,7 @@ struct DecodeArgs {
 hipError_t launch_plan(const int32_t* seqlens, int batch, int rows, int num_parts, int32_t* tile_md,
                        int32_t* num_splits, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_wide(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace mla

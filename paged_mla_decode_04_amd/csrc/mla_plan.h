@@ -40,14 +40,16 @@ namespace mla {
 
 constexpr int kPageTokens = 64;
 constexpr int kTileMdInts = 8;
-constexpr int kRowsPerWorkgroup = 64;
+constexpr int kRowsPerWorkgroup = 128;
 constexpr int kMaxPlanBatch = 16384;  // device plan keeps the prefix sums in LDS
 
-// Rows one workgroup handles when the kv head has `rows` query rows: up to 4
-// compute waves of 16 rows.
+// Rows one workgroup handles when the kv head has `rows` query rows: 16, 32
+// or 64 (the narrow kernel, up to 4 score tiles of 16 rows), else 128 (the
+// wide kernel).
 MLA_HD inline int rows_per_block(int rows) {
   if (rows <= 16) return 16;
   if (rows <= 32) return 32;
+  if (rows <= 64) return 64;
   return kRowsPerWorkgroup;
 }
 

@@ -30,7 +30,7 @@ def units(n):
 
 
 def seg_cost(q_rows):
-    r = 16 if q_rows <= 16 else 32 if q_rows <= 32 else 64
+    r = 16 if q_rows <= 16 else 32 if q_rows <= 32 else 64 if q_rows <= 64 else 128
     return max(1, (r + 27) // 28)
 
 
