@@ -7,8 +7,10 @@ hipcc cross-compiles the device code without a GPU present.
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -28,6 +30,39 @@ HIPCC_FLAGS = [
 def hipcc() -> str:
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
     return os.path.join(rocm, "bin", "hipcc")
+
+
+# Kernels whose output accumulators live in fixed AGPRs that only inline
+# assembly touches: the compiler must not use any AGPR itself there (it would
+# spill into them and overwrite the accumulators).
+FIXED_AGPR_SOURCES = ["mla_decode_wide.hip"]
+_ASM_AGPR = re.compile(r"accvgpr|\ba\[\d|[ ,]a\d+\b")
+
+
+def check_fixed_agprs(src: str) -> None:
+    """Fail if the compiler itself references AGPRs in the kernel's assembly."""
+    with tempfile.TemporaryDirectory() as td:
+        out = os.path.join(td, "k.s")
+        cmd = [hipcc(), *HIPCC_FLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out]
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc -S failed for {src}:\n" + r.stdout.decode(errors="replace"))
+        in_asm = False
+        bad = []
+        with open(out) as f:
+            for line in f:
+                if ";;#ASMSTART" in line:
+                    in_asm = True
+                    continue
+                if ";;#ASMEND" in line:
+                    in_asm = False
+                    continue
+                code = line.split(";", 1)[0]
+                if not in_asm and code.startswith("\t") and _ASM_AGPR.search(code):
+                    bad.append(code.strip())
+        if bad:
+            raise RuntimeError(f"{src}: the compiler uses AGPRs reserved for the accumulators "
+                               f"(register pressure too high?): {bad[:4]}")
 
 
 def build(verbose: bool = False) -> str:
@@ -54,6 +89,16 @@ def build(verbose: bool = False) -> str:
         if os.path.exists(LIB_PATH):
             os.remove(LIB_PATH)
         raise RuntimeError("hipcc failed:\n" + "\n".join(failed))
+    try:
+        for src in FIXED_AGPR_SOURCES:
+            check_fixed_agprs(src)
+    except RuntimeError:
+        if os.path.exists(LIB_PATH):
+            os.remove(LIB_PATH)
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
+        raise
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)

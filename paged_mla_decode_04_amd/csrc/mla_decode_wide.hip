@@ -1,5 +1,6 @@
-// Split-KV decode for the wide-head shape: up to 128 query rows per kv head in
-// one workgroup, so that every cached token is read from HBM once per part.
+// Split-KV decode for the wide-head shape: up to 128 query rows of one kv
+// head per workgroup, so that every cached token is read from HBM once per
+// part.
 //
 // What is computed is the same as for the narrow kernel (mla_kernels.hip):
 // for each query row r = (query token i, head h), softmax(scale * q_r . k_t)
@@ -9,34 +10,37 @@
 // states the inputs and prices the work as (d + dv) multiply-adds per
 // query-key pair and one d-element read per cached token.
 //
-// Layout of the work on gfx950 (one workgroup of 4 waves per CU, one wave per
-// SIMD, each wave with the SIMD's whole register file):
-//   * wave w holds the queries of rows 32 w .. 32 w + 31 (two 16-row tiles,
-//     144 registers) and computes their scores S^T = K . Q^T for all 32 tokens
-//     of a chunk on 16x16x32 bf16 MFMA -- every 16-byte K fragment read from
-//     LDS feeds two MFMAs;
-//   * wave w owns the softmax state of those rows.  It sees every score of a
-//     row, so it moves the row's reference max itself when a chunk passes it
-//     and writes P (bf16) to LDS already in the B-operand layout of the value
-//     product;
-//   * wave w also owns output columns 128 w .. 128 w + 127 of all 128 rows
-//     (256 accumulator registers) and accumulates O^T += V^T . P^T, reading
-//     V^T with the transposing LDS read ds_read_b64_tr_b16, so V is read from
-//     LDS once per workgroup;
-//   * when a wave moved the reference of its rows it leaves the rescale
-//     factors in LDS and a flag; the next step every wave rescales those rows
-//     of its accumulators before adding the next chunk.
-// In step t the waves compute the scores and P of chunk t + 1 and the values
-// of chunk t; the copy of chunk t + 2 lands and that of chunk t + 3 is issued.
-// A chunk's latent part (32 tokens x 512 columns) lives in one of four 32 KB
-// slots (read for the scores one step, for the values the next), its rope
-// part (32 x 64) in one of three 4 KB slots (read for the scores only).
-// One workgroup barrier per step.
+// Layout of the work on gfx950: one workgroup of 4 waves per CU, one wave per
+// SIMD with the SIMD's whole register file.  Wave w owns query rows
+// 32 w .. 32 w + 31 from end to end:
+//   * its queries stay in 144 VGPRs as the B operand of the scores
+//     S^T = K . Q^T, one 32x32x16 bf16 MFMA per 16 columns of d (36 per
+//     32-token chunk, one accumulator chain: the matrix core forwards the
+//     accumulator, so the chain runs at the full rate);
+//   * in the 32x32 result each lane holds one query row and 16 of the
+//     chunk's 32 tokens, so the softmax needs no cross-lane step except when
+//     the reference max moves, and P (bf16) is already the B operand of the
+//     value product, lane for lane, for the token order the transposing V
+//     read produces;
+//   * its output rows, O^T = V^T . P^T for all 512 columns, are 16 32x32
+//     tiles in the 256 accumulation registers, one MFMA per tile per 16
+//     tokens (32 per chunk), V^T read with ds_read_b64_tr_b16.
+// Nothing but the cached chunks goes through LDS: no wave waits for another
+// except at the one barrier per step that recycles chunk slots.
 //
-// LDS slot layout: latent block (r, q) = tokens 8r..8r+7 x columns 64q..64q+63
-// at 8192 r + 1024 q, rope block r at 1024 r; inside a block token a sits at
-// 128 a and its 16-byte column chunk c at slot (c ^ a ^ 2 (r & 1)), the same
-// conflict-free swizzle as the narrow kernel.
+// Step t scores chunk t + 1 and accumulates the values of chunk t, with the
+// softmax of chunk t + 1 issued between the value MFMAs; the copy of chunk
+// t + 3 is issued between the score MFMAs and lands by the end of step t + 1.
+// A step whose score chunk starts a new sequence loads that sequence's
+// queries first and runs its value product before the scores, which hides the
+// load behind it.
+//
+// LDS: four slots of one 32-token chunk (32 x 576 bf16 = 36 KB): column block
+// q (64 columns) of the chunk at 4096 q, token a at 128 a inside it, its
+// 16-byte column chunk c (0..7) at slot c ^ swz(a).  The swizzle keeps the
+// score reads (32 tokens x one chunk per 512 bytes) and the transposing value
+// reads (4 tokens x 4 chunks per 256 bytes) at two and one pass over the
+// banks.
 #include <type_traits>
 
 #include "mla_device.h"
@@ -44,112 +48,25 @@
 namespace mla {
 namespace {
 
-constexpr int kThreadsW = 256;                          // 4 waves, one per SIMD
-constexpr int kRowsW = 128;                             // query rows per workgroup
-constexpr int kRowTiles = kRowsW / 16;                  // 8
-constexpr int kLatBytes = kChunk * kDv * 2;             // 32768
-constexpr int kRopeBytes = kChunk * (kD - kDv) * 2;     // 4096
-constexpr int kLatSlots = 4, kRopeSlots = 3;
-constexpr int kRopeOff = kLatSlots * kLatBytes;                 // 131072
-constexpr int kPOff = kRopeOff + kRopeSlots * kRopeBytes;       // P^T: [parity][row tile][lane] x 16 B
-constexpr int kFacOff = kPOff + 2 * kRowTiles * 1024;           // rescale factors: [parity][row] f32
-constexpr int kFinOff = kFacOff + 2 * kRowsW * 4;               // segment results: [segment parity][inv, lse][row]
-constexpr int kFlagOff = kFinOff + 2 * 2 * kRowsW * 4;          // reference moved: [parity][wave] int
-constexpr int kSmemW = kFlagOff + 2 * 4 * 4;
+constexpr int kThreadsW = 256;                    // 4 waves, one per SIMD
+constexpr int kRowsW = 128;                       // query rows per workgroup
+constexpr int kTileBytes = kChunk * kD * 2;       // 36864
+constexpr int kSlots = 4;
+constexpr int kSmemW = kSlots * kTileBytes;       // 147456
+constexpr int kSSteps = kD / 16;                  // 36 score k-steps
+constexpr int kColTiles = kDv / 32;               // 16 output column tiles
+constexpr int kCopiesW = 9;                       // 1 KB copies per wave per chunk
+constexpr int kKAhead = 7;                        // score K fragments in flight
+constexpr int kVAhead = 6;                        // value V^T fragments in flight
 static_assert(kSmemW <= 160 * 1024, "LDS budget");
-static_assert(kKSteps == 18, "16 latent k-steps + 2 rope k-steps");
-constexpr int kCopyLoadsW = 9;  // 1 KB LDS-direct loads per wave per chunk
-constexpr int kKAheadW = 2;     // k-steps of K fragments in flight
+static_assert(kThreadsW / 64 * kCopiesW * 1024 == kTileBytes, "copies cover the chunk");
 
-// Wave w copies the blocks of its own value columns, latent blocks (r, 2w) and
-// (r, 2w + 1) for r = 0..3, and rope block w: 9 KB of the chunk's 36 KB, as
-// nine 1 KB LDS-direct loads.
-// Lane l moves 16 bytes of token row 8 r + (l >> 3); its byte offset is
-// A[r & 1] + 8 r * row_bytes (+ 128 for the second column block), with the
-// lane constants A[p] = (l >> 3) * row_bytes + 16 ((l & 7) ^ (l >> 3) ^ 2p) +
-// 256 w -- the swizzled source chunk that lands at the lane's LDS slot.
-struct CopyPlan {
-  __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t lat, rope;  // LDS destinations: this wave's latent blocks, its rope block
-  uint32_t rb8;        // 8 rows in bytes
-  bool on;             // the chunk has keys to copy
-};
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-__device__ __forceinline__ CopyPlan copy_plan(const DecodeArgs& a, const Chunk& c, uint32_t lat, uint32_t rope,
-                                              int w) {
-  CopyPlan p;
-  p.on = c.valid() && c.tok > 0;
-  p.rsrc = chunk_rsrc(a, c);
-  p.lat = lat + 2048u * w;
-  p.rope = rope + 1024u * w;
-  p.rb8 = 8u * (uint32_t)a.k_row_bytes;
-  return p;
-}
+// Swizzle of token a's eight 16-byte chunks in a column block (uses bits 1..3
+// of a, so it repeats every 16 tokens).
+__device__ __forceinline__ int swz(int a) { return (((a >> 1) & 1) << 2) | ((a >> 2) & 3); }
 
-// Load k (0..8) of the wave's share: latent block (k >> 1, 2w + (k & 1)), or
-// for k = 8 the rope block.
-template <int K>
-__device__ __forceinline__ void copy_one(const CopyPlan& p, int w, uint32_t a0, uint32_t a1) {
-  if constexpr (K < 8) {
-    constexpr int r = K >> 1, h = K & 1;
-    const uint32_t v = ((r & 1) ? a1 : a0) + (uint32_t)r * p.rb8 + 128u * h;
-    lds_dma16(p.rsrc, v, p.lat + 8192u * r + 1024u * h);
-  } else {
-    // rope block w: row 8 w + (l >> 3), byte 1024 + 16 (swizzled chunk)
-    const uint32_t v = ((w & 1) ? a1 : a0) + (uint32_t)w * (p.rb8 - 256u) + 1024u;
-    lds_dma16(p.rsrc, v, p.rope);
-  }
-}
-
-__device__ __forceinline__ bool wide_copy(const DecodeArgs& a, const Chunk& c, uint32_t lat, uint32_t rope, int w,
-                                          uint32_t a0, uint32_t a1) {
-  const CopyPlan p = copy_plan(a, c, lat, rope, w);
-  if (!p.on) return false;
-  copy_one<0>(p, w, a0, a1);
-  copy_one<1>(p, w, a0, a1);
-  copy_one<2>(p, w, a0, a1);
-  copy_one<3>(p, w, a0, a1);
-  copy_one<4>(p, w, a0, a1);
-  copy_one<5>(p, w, a0, a1);
-  copy_one<6>(p, w, a0, a1);
-  copy_one<7>(p, w, a0, a1);
-  copy_one<8>(p, w, a0, a1);
-  return true;
-}
-
-// An opaque copy of the lane index: lane-derived offsets computed from it in
-// one section of the step are not merged with (and kept live until) those of
-// another.
-__device__ __forceinline__ int fresh_lane(int lane) {
-  asm volatile("" : "+v"(lane));
-  return lane;
-}
-
-// Per-lane offsets of the operand reads and of the copy.  Rebuilt from the
-// lane index every step: the loop keeps the queries (144 VGPRs) and the value
-// accumulators (256 AGPRs) resident and cannot afford to hold these too.
-struct LaneMap {
-  int g, r16;
-  uint32_t kx, k_lat, k_rope;  // score K fragment: token 16 tt + r16, column chunk 4 ks + g
-  uint32_t vy, v_lane;         // value V^T fragment (transposing read)
-  uint32_t cp0, cp1;           // copy source offsets A[0], A[1]
-  __device__ __forceinline__ LaneMap(int lane, int w, uint32_t row_bytes) {
-    g = lane >> 4;
-    r16 = lane & 15;
-    const int ka = r16 & 7, kr = r16 >> 3;
-    kx = (uint32_t)(g ^ ka ^ (2 * kr));
-    k_lat = 8192u * kr + 128u * ka;
-    k_rope = 1024u * kr + 128u * ka;
-    const int va = 4 * (g & 1) + (r16 >> 2);
-    vy = (uint32_t)(((r16 & 3) >> 1) ^ va ^ (2 * ((g >> 1) & 1)));
-    v_lane = 8192u * (g >> 1) + 1024u * (2 * w) + 128u * va + 8u * (r16 & 1);
-    const int ta = lane >> 3, te = lane & 7;
-    cp0 = (uint32_t)ta * row_bytes + 16u * (uint32_t)(te ^ ta) + 256u * w;
-    cp1 = (uint32_t)ta * row_bytes + 16u * (uint32_t)(te ^ ta ^ 2) + 256u * w;
-  }
-};
-
-// f(std::integral_constant<int, I>{}) for I = B .. E - 1, unrolled by construction
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
   if constexpr (B < E) {
@@ -158,61 +75,188 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// Compiler fence between the sections of a step: the next section's LDS reads
-// (and the registers they fill) stay behind it instead of being hoisted ahead
-// of the previous section's MFMAs.
-__device__ __forceinline__ void section_fence() { asm volatile("" ::: "memory"); }
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 
-// One k-step of the scores, s[tt][rl] += K_tt . Q_rl^T, as four MFMAs with
-// VGPR accumulators.  Written as assembly so that the score accumulators stay
-// in VGPRs while the value accumulators fill all 256 AGPRs (the compiler puts
-// every MFMA result of a function in one register file).  The k-step
-// fragments come straight from LDS and global loads; the first k-step starts
-// from zero (no VALU write feeds an MFMA here), and consecutive MFMAs on one
-// accumulator are three MFMAs apart.
-__device__ __forceinline__ void score_mfma(f32x4 (&s)[2][2], bf16x8 k0, bf16x8 k1, bf16x8 q0, bf16x8 q1,
-                                           bool first) {
+// s (+)= K . Q^T for one 16-column step of d; the accumulator stays in VGPRs
+// (written as assembly: the compiler would put every MFMA result of the
+// kernel in the register file the value accumulators fill).  The compiler
+// does not see an MFMA here, so the two wait states an operand written by a
+// VALU move needs are part of it.
+__device__ __forceinline__ void score_mfma(f32x16& s, bf16x8 k, bf16x8 q, bool first) {
   if (first)
-    asm("s_nop 4\n\t"
-        "v_mfma_f32_16x16x32_bf16 %0, %4, %6, 0\n\t"
-        "v_mfma_f32_16x16x32_bf16 %1, %4, %7, 0\n\t"
-        "v_mfma_f32_16x16x32_bf16 %2, %5, %6, 0\n\t"
-        "v_mfma_f32_16x16x32_bf16 %3, %5, %7, 0"
-        : "=&v"(s[0][0]), "=&v"(s[0][1]), "=&v"(s[1][0]), "=&v"(s[1][1])
-        : "v"(k0), "v"(k1), "v"(q0), "v"(q1));
+    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(k), "v"(q));
   else
-    asm("v_mfma_f32_16x16x32_bf16 %0, %4, %6, %0\n\t"
-        "v_mfma_f32_16x16x32_bf16 %1, %4, %7, %1\n\t"
-        "v_mfma_f32_16x16x32_bf16 %2, %5, %6, %2\n\t"
-        "v_mfma_f32_16x16x32_bf16 %3, %5, %7, %3"
-        : "+v"(s[0][0]), "+v"(s[0][1]), "+v"(s[1][0]), "+v"(s[1][1])
-        : "v"(k0), "v"(k1), "v"(q0), "v"(q1));
+    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(k), "v"(q));
 }
 
-// The score accumulators are read by VALU instructions next: wait out the
-// MFMA result latency (more than the 8-pass requirement) first.
-__device__ __forceinline__ void score_done(f32x4 (&s)[2][2]) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
-               : "+v"(s[0][0]), "+v"(s[0][1]), "+v"(s[1][0]), "+v"(s[1][1]));
+// ---- the output accumulators: fixed AGPRs, a[16 ct .. 16 ct + 15] for tile
+// ct, touched only by the assembly below (the compiler never holds them, so
+// it cannot copy or spill them; the zeroing names every one of them as
+// clobbered, which reserves all 256 for the kernel).
+// (the compiler does not see these as MFMAs: the two wait states cover an
+// operand it may have just assembled with VALU moves)
+#define MLA_VMFMA(LO, HI) \
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[" #LO ":" #HI "], %0, %1, a[" #LO ":" #HI "]" ::"v"(v), "v"(p))
+template <int CT>
+__device__ __forceinline__ void value_mfma(bf16x8 v, bf16x8 p) {
+  if constexpr (CT == 0) MLA_VMFMA(0, 15);
+  else if constexpr (CT == 1) MLA_VMFMA(16, 31);
+  else if constexpr (CT == 2) MLA_VMFMA(32, 47);
+  else if constexpr (CT == 3) MLA_VMFMA(48, 63);
+  else if constexpr (CT == 4) MLA_VMFMA(64, 79);
+  else if constexpr (CT == 5) MLA_VMFMA(80, 95);
+  else if constexpr (CT == 6) MLA_VMFMA(96, 111);
+  else if constexpr (CT == 7) MLA_VMFMA(112, 127);
+  else if constexpr (CT == 8) MLA_VMFMA(128, 143);
+  else if constexpr (CT == 9) MLA_VMFMA(144, 159);
+  else if constexpr (CT == 10) MLA_VMFMA(160, 175);
+  else if constexpr (CT == 11) MLA_VMFMA(176, 191);
+  else if constexpr (CT == 12) MLA_VMFMA(192, 207);
+  else if constexpr (CT == 13) MLA_VMFMA(208, 223);
+  else if constexpr (CT == 14) MLA_VMFMA(224, 239);
+  else if constexpr (CT == 15) MLA_VMFMA(240, 255);
 }
+#undef MLA_VMFMA
 
-// One MFMA of the values, o += V^T_ct . P^T_rt, accumulating in AGPRs.
-// Assembly for the same reason as the scores.  A new V fragment may have been
-// assembled by VALU moves, hence the wait states before its first MFMA.  Each
-// accumulator gets one MFMA per step.
-__device__ __forceinline__ void value_mfma1(f32x4& o, bf16x8 v, bf16x8 p, bool new_v) {
-  if (new_v)
-    asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(v), "v"(p));
-  else
-    asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(v), "v"(p));
+#define MLA_AREAD4(A, B, C, D)                                                                 \
+  asm volatile("v_accvgpr_read_b32 %0, a" #A "\n\tv_accvgpr_read_b32 %1, a" #B                  \
+               "\n\tv_accvgpr_read_b32 %2, a" #C "\n\tv_accvgpr_read_b32 %3, a" #D             \
+               : "=v"(x0), "=v"(x1), "=v"(x2), "=v"(x3))
+// Accumulators a[4 I .. 4 I + 3] (elements 4 g .. 4 g + 3 of tile ct at I = 4 ct + g).
+template <int I>
+__device__ __forceinline__ f32x4 acc_read4() {
+  float x0, x1, x2, x3;
+  if constexpr (I == 0) MLA_AREAD4(0, 1, 2, 3);
+  else if constexpr (I == 1) MLA_AREAD4(4, 5, 6, 7);
+  else if constexpr (I == 2) MLA_AREAD4(8, 9, 10, 11);
+  else if constexpr (I == 3) MLA_AREAD4(12, 13, 14, 15);
+  else if constexpr (I == 4) MLA_AREAD4(16, 17, 18, 19);
+  else if constexpr (I == 5) MLA_AREAD4(20, 21, 22, 23);
+  else if constexpr (I == 6) MLA_AREAD4(24, 25, 26, 27);
+  else if constexpr (I == 7) MLA_AREAD4(28, 29, 30, 31);
+  else if constexpr (I == 8) MLA_AREAD4(32, 33, 34, 35);
+  else if constexpr (I == 9) MLA_AREAD4(36, 37, 38, 39);
+  else if constexpr (I == 10) MLA_AREAD4(40, 41, 42, 43);
+  else if constexpr (I == 11) MLA_AREAD4(44, 45, 46, 47);
+  else if constexpr (I == 12) MLA_AREAD4(48, 49, 50, 51);
+  else if constexpr (I == 13) MLA_AREAD4(52, 53, 54, 55);
+  else if constexpr (I == 14) MLA_AREAD4(56, 57, 58, 59);
+  else if constexpr (I == 15) MLA_AREAD4(60, 61, 62, 63);
+  else if constexpr (I == 16) MLA_AREAD4(64, 65, 66, 67);
+  else if constexpr (I == 17) MLA_AREAD4(68, 69, 70, 71);
+  else if constexpr (I == 18) MLA_AREAD4(72, 73, 74, 75);
+  else if constexpr (I == 19) MLA_AREAD4(76, 77, 78, 79);
+  else if constexpr (I == 20) MLA_AREAD4(80, 81, 82, 83);
+  else if constexpr (I == 21) MLA_AREAD4(84, 85, 86, 87);
+  else if constexpr (I == 22) MLA_AREAD4(88, 89, 90, 91);
+  else if constexpr (I == 23) MLA_AREAD4(92, 93, 94, 95);
+  else if constexpr (I == 24) MLA_AREAD4(96, 97, 98, 99);
+  else if constexpr (I == 25) MLA_AREAD4(100, 101, 102, 103);
+  else if constexpr (I == 26) MLA_AREAD4(104, 105, 106, 107);
+  else if constexpr (I == 27) MLA_AREAD4(108, 109, 110, 111);
+  else if constexpr (I == 28) MLA_AREAD4(112, 113, 114, 115);
+  else if constexpr (I == 29) MLA_AREAD4(116, 117, 118, 119);
+  else if constexpr (I == 30) MLA_AREAD4(120, 121, 122, 123);
+  else if constexpr (I == 31) MLA_AREAD4(124, 125, 126, 127);
+  else if constexpr (I == 32) MLA_AREAD4(128, 129, 130, 131);
+  else if constexpr (I == 33) MLA_AREAD4(132, 133, 134, 135);
+  else if constexpr (I == 34) MLA_AREAD4(136, 137, 138, 139);
+  else if constexpr (I == 35) MLA_AREAD4(140, 141, 142, 143);
+  else if constexpr (I == 36) MLA_AREAD4(144, 145, 146, 147);
+  else if constexpr (I == 37) MLA_AREAD4(148, 149, 150, 151);
+  else if constexpr (I == 38) MLA_AREAD4(152, 153, 154, 155);
+  else if constexpr (I == 39) MLA_AREAD4(156, 157, 158, 159);
+  else if constexpr (I == 40) MLA_AREAD4(160, 161, 162, 163);
+  else if constexpr (I == 41) MLA_AREAD4(164, 165, 166, 167);
+  else if constexpr (I == 42) MLA_AREAD4(168, 169, 170, 171);
+  else if constexpr (I == 43) MLA_AREAD4(172, 173, 174, 175);
+  else if constexpr (I == 44) MLA_AREAD4(176, 177, 178, 179);
+  else if constexpr (I == 45) MLA_AREAD4(180, 181, 182, 183);
+  else if constexpr (I == 46) MLA_AREAD4(184, 185, 186, 187);
+  else if constexpr (I == 47) MLA_AREAD4(188, 189, 190, 191);
+  else if constexpr (I == 48) MLA_AREAD4(192, 193, 194, 195);
+  else if constexpr (I == 49) MLA_AREAD4(196, 197, 198, 199);
+  else if constexpr (I == 50) MLA_AREAD4(200, 201, 202, 203);
+  else if constexpr (I == 51) MLA_AREAD4(204, 205, 206, 207);
+  else if constexpr (I == 52) MLA_AREAD4(208, 209, 210, 211);
+  else if constexpr (I == 53) MLA_AREAD4(212, 213, 214, 215);
+  else if constexpr (I == 54) MLA_AREAD4(216, 217, 218, 219);
+  else if constexpr (I == 55) MLA_AREAD4(220, 221, 222, 223);
+  else if constexpr (I == 56) MLA_AREAD4(224, 225, 226, 227);
+  else if constexpr (I == 57) MLA_AREAD4(228, 229, 230, 231);
+  else if constexpr (I == 58) MLA_AREAD4(232, 233, 234, 235);
+  else if constexpr (I == 59) MLA_AREAD4(236, 237, 238, 239);
+  else if constexpr (I == 60) MLA_AREAD4(240, 241, 242, 243);
+  else if constexpr (I == 61) MLA_AREAD4(244, 245, 246, 247);
+  else if constexpr (I == 62) MLA_AREAD4(248, 249, 250, 251);
+  else if constexpr (I == 63) MLA_AREAD4(252, 253, 254, 255);
+  return f32x4{x0, x1, x2, x3};
 }
+#undef MLA_AREAD4
 
-// The accumulators of one row tile are about to be read or written by VALU
-// instructions: wait out the result latency of the MFMAs that wrote them.
-__device__ __forceinline__ void acc_ready(f32x4 (&o)[8]) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
-               : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]), "+a"(o[6]), "+a"(o[7]));
+#define MLA_AZERO4(A, B, C, D)                                                                 \
+  asm volatile("v_accvgpr_write_b32 a" #A ", 0\n\tv_accvgpr_write_b32 a" #B ", 0\n\t"            \
+               "v_accvgpr_write_b32 a" #C ", 0\n\tv_accvgpr_write_b32 a" #D ", 0" ::                \
+                   : "a" #A, "a" #B, "a" #C, "a" #D)
+// Every accumulator to zero.
+__device__ __forceinline__ void acc_zero() {
+  MLA_AZERO4(0, 1, 2, 3); MLA_AZERO4(4, 5, 6, 7); MLA_AZERO4(8, 9, 10, 11); MLA_AZERO4(12, 13, 14, 15);
+  MLA_AZERO4(16, 17, 18, 19); MLA_AZERO4(20, 21, 22, 23); MLA_AZERO4(24, 25, 26, 27); MLA_AZERO4(28, 29, 30, 31);
+  MLA_AZERO4(32, 33, 34, 35); MLA_AZERO4(36, 37, 38, 39); MLA_AZERO4(40, 41, 42, 43); MLA_AZERO4(44, 45, 46, 47);
+  MLA_AZERO4(48, 49, 50, 51); MLA_AZERO4(52, 53, 54, 55); MLA_AZERO4(56, 57, 58, 59); MLA_AZERO4(60, 61, 62, 63);
+  MLA_AZERO4(64, 65, 66, 67); MLA_AZERO4(68, 69, 70, 71); MLA_AZERO4(72, 73, 74, 75); MLA_AZERO4(76, 77, 78, 79);
+  MLA_AZERO4(80, 81, 82, 83); MLA_AZERO4(84, 85, 86, 87); MLA_AZERO4(88, 89, 90, 91); MLA_AZERO4(92, 93, 94, 95);
+  MLA_AZERO4(96, 97, 98, 99); MLA_AZERO4(100, 101, 102, 103); MLA_AZERO4(104, 105, 106, 107); MLA_AZERO4(108, 109, 110, 111);
+  MLA_AZERO4(112, 113, 114, 115); MLA_AZERO4(116, 117, 118, 119); MLA_AZERO4(120, 121, 122, 123); MLA_AZERO4(124, 125, 126, 127);
+  MLA_AZERO4(128, 129, 130, 131); MLA_AZERO4(132, 133, 134, 135); MLA_AZERO4(136, 137, 138, 139); MLA_AZERO4(140, 141, 142, 143);
+  MLA_AZERO4(144, 145, 146, 147); MLA_AZERO4(148, 149, 150, 151); MLA_AZERO4(152, 153, 154, 155); MLA_AZERO4(156, 157, 158, 159);
+  MLA_AZERO4(160, 161, 162, 163); MLA_AZERO4(164, 165, 166, 167); MLA_AZERO4(168, 169, 170, 171); MLA_AZERO4(172, 173, 174, 175);
+  MLA_AZERO4(176, 177, 178, 179); MLA_AZERO4(180, 181, 182, 183); MLA_AZERO4(184, 185, 186, 187); MLA_AZERO4(188, 189, 190, 191);
+  MLA_AZERO4(192, 193, 194, 195); MLA_AZERO4(196, 197, 198, 199); MLA_AZERO4(200, 201, 202, 203); MLA_AZERO4(204, 205, 206, 207);
+  MLA_AZERO4(208, 209, 210, 211); MLA_AZERO4(212, 213, 214, 215); MLA_AZERO4(216, 217, 218, 219); MLA_AZERO4(220, 221, 222, 223);
+  MLA_AZERO4(224, 225, 226, 227); MLA_AZERO4(228, 229, 230, 231); MLA_AZERO4(232, 233, 234, 235); MLA_AZERO4(236, 237, 238, 239);
+  MLA_AZERO4(240, 241, 242, 243); MLA_AZERO4(244, 245, 246, 247); MLA_AZERO4(248, 249, 250, 251); MLA_AZERO4(252, 253, 254, 255);
 }
+#undef MLA_AZERO4
+
+#define MLA_ASCALE4(A, B, C, D)                                                                \
+  asm volatile("v_accvgpr_read_b32 %0, a" #A "\n\tv_accvgpr_read_b32 %1, a" #B "\n\t"               \
+               "v_accvgpr_read_b32 %2, a" #C "\n\tv_accvgpr_read_b32 %3, a" #D "\n\t"               \
+               "v_mul_f32 %0, %0, %4\n\tv_mul_f32 %1, %1, %4\n\t"                                  \
+               "v_mul_f32 %2, %2, %4\n\tv_mul_f32 %3, %3, %4\n\t"                                  \
+               "v_accvgpr_write_b32 a" #A ", %0\n\tv_accvgpr_write_b32 a" #B ", %1\n\t"              \
+               "v_accvgpr_write_b32 a" #C ", %2\n\tv_accvgpr_write_b32 a" #D ", %3"                    \
+               : "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3)                                    \
+               : "v"(f))
+// Every accumulator times this lane's factor f.
+__device__ __forceinline__ void acc_scale(float f) {
+  float t0, t1, t2, t3;
+  MLA_ASCALE4(0, 1, 2, 3); MLA_ASCALE4(4, 5, 6, 7); MLA_ASCALE4(8, 9, 10, 11); MLA_ASCALE4(12, 13, 14, 15);
+  MLA_ASCALE4(16, 17, 18, 19); MLA_ASCALE4(20, 21, 22, 23); MLA_ASCALE4(24, 25, 26, 27); MLA_ASCALE4(28, 29, 30, 31);
+  MLA_ASCALE4(32, 33, 34, 35); MLA_ASCALE4(36, 37, 38, 39); MLA_ASCALE4(40, 41, 42, 43); MLA_ASCALE4(44, 45, 46, 47);
+  MLA_ASCALE4(48, 49, 50, 51); MLA_ASCALE4(52, 53, 54, 55); MLA_ASCALE4(56, 57, 58, 59); MLA_ASCALE4(60, 61, 62, 63);
+  MLA_ASCALE4(64, 65, 66, 67); MLA_ASCALE4(68, 69, 70, 71); MLA_ASCALE4(72, 73, 74, 75); MLA_ASCALE4(76, 77, 78, 79);
+  MLA_ASCALE4(80, 81, 82, 83); MLA_ASCALE4(84, 85, 86, 87); MLA_ASCALE4(88, 89, 90, 91); MLA_ASCALE4(92, 93, 94, 95);
+  MLA_ASCALE4(96, 97, 98, 99); MLA_ASCALE4(100, 101, 102, 103); MLA_ASCALE4(104, 105, 106, 107); MLA_ASCALE4(108, 109, 110, 111);
+  MLA_ASCALE4(112, 113, 114, 115); MLA_ASCALE4(116, 117, 118, 119); MLA_ASCALE4(120, 121, 122, 123); MLA_ASCALE4(124, 125, 126, 127);
+  MLA_ASCALE4(128, 129, 130, 131); MLA_ASCALE4(132, 133, 134, 135); MLA_ASCALE4(136, 137, 138, 139); MLA_ASCALE4(140, 141, 142, 143);
+  MLA_ASCALE4(144, 145, 146, 147); MLA_ASCALE4(148, 149, 150, 151); MLA_ASCALE4(152, 153, 154, 155); MLA_ASCALE4(156, 157, 158, 159);
+  MLA_ASCALE4(160, 161, 162, 163); MLA_ASCALE4(164, 165, 166, 167); MLA_ASCALE4(168, 169, 170, 171); MLA_ASCALE4(172, 173, 174, 175);
+  MLA_ASCALE4(176, 177, 178, 179); MLA_ASCALE4(180, 181, 182, 183); MLA_ASCALE4(184, 185, 186, 187); MLA_ASCALE4(188, 189, 190, 191);
+  MLA_ASCALE4(192, 193, 194, 195); MLA_ASCALE4(196, 197, 198, 199); MLA_ASCALE4(200, 201, 202, 203); MLA_ASCALE4(204, 205, 206, 207);
+  MLA_ASCALE4(208, 209, 210, 211); MLA_ASCALE4(212, 213, 214, 215); MLA_ASCALE4(216, 217, 218, 219); MLA_ASCALE4(220, 221, 222, 223);
+  MLA_ASCALE4(224, 225, 226, 227); MLA_ASCALE4(228, 229, 230, 231); MLA_ASCALE4(232, 233, 234, 235); MLA_ASCALE4(236, 237, 238, 239);
+  MLA_ASCALE4(240, 241, 242, 243); MLA_ASCALE4(244, 245, 246, 247); MLA_ASCALE4(248, 249, 250, 251); MLA_ASCALE4(252, 253, 254, 255);
+}
+#undef MLA_ASCALE4
+
+// The MFMA results about to be read by VALU instructions: wait out the result
+// latency of a 32x32 MFMA (more than its 18 required wait states).
+__device__ __forceinline__ void mfma_result_wait() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
 
 // Chunk descriptors in batches of 64.  Every wave computes the descriptors of
 // the next 64 chunks of its part lane-parallel (lane i: chunk position + i),
@@ -302,6 +346,7 @@ __device__ __forceinline__ Chunk batch_get(const i32x4& b, int i) {
   return c;
 }
 
+
 __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmemW];
   const int w = uniform(threadIdx.x >> 6);
@@ -311,55 +356,285 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
 
   lds_u8* const lds = (lds_u8*)smem;
   const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
-  lds_f32* const fac = (lds_f32*)(lds + kFacOff);
-  lds_f32* const fin = (lds_f32*)(lds + kFinOff);
-  lds_i32* const flags = (lds_i32*)(lds + kFlagOff);
   const uint32_t row_bytes = (uint32_t)a.k_row_bytes;
   const float sc = a.scale_log2;
 
-  // ---- scores and softmax: rows 32 w + 16 rl + r16 (reference max m_ref in
-  // log2 units, running sum of 2^(x - m_ref) per lane over its tokens)
-  bf16x8 qf[2][kKSteps];
-  float m_ref[2] = {-INFINITY, -INFINITY};
-  float lsum[2] = {0.f, 0.f};
-  int lim_min = 0;  // smallest visible-key limit among this wave's rows
-  int seg_n = 0;    // cached tokens of the scores' segment (after the cap)
-  // ---- values: columns 128 w + 16 ct + 4 g + j of rows 16 rt + r16
-  f32x4 o[kRowTiles][8];
-#pragma unroll
-  for (int rt = 0; rt < kRowTiles; ++rt)
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) o[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // this lane's query row (the same in the scores and the values), rebuilt
+  // from an opaque lane index where it is used
+  const int hlf = lane >> 5;
+  struct RowInfo {
+    int row, qi, hh;
+    bool ok;
+  };
+  auto row_info = [&]() -> RowInfo {
+    RowInfo r;
+    r.row = pi.blk_row0 + 32 * w + (opaque(lane) & 31);
+    r.ok = r.row < a.rows;
+    const int rr = r.ok ? r.row : 0;
+    r.qi = rr / a.h_q;
+    r.hh = rr - r.qi * a.h_q;
+    return r;
+  };
+  const bool wave_full = pi.blk_row0 + 32 * w + 32 <= a.rows;
+  const int qi_min = (pi.blk_row0 + 32 * w) / a.h_q;
+
+  // ---- per-lane LDS offsets inside a slot, recomputed where used from an
+  // opaque copy of the lane index (holding them would cost 8 VGPRs)
+  // score K fragment of k-step ks (u = ks & 3): token j32, 16-byte chunk 2 ks + hlf
+  auto koff = [](int ln, int u) -> uint32_t {
+    const int j = ln & 31, hb = ln >> 5;
+    return 128u * j + 16u * ((2 * u + hb) ^ swz(j));
+  };
+  // value V^T half fragment (ct & 1 = cb, b): 16-lane group G reads tokens
+  // 8 b + 4 (G >> 1) + 0..3 of the k-step, columns 16 (G & 1) + 0..15 of the tile
+  auto voff = [](int ln, int cb, int b) -> uint32_t {
+    const int G = ln >> 4, s16 = ln & 15;
+    const int tl = 8 * b + 4 * (G >> 1) + (s16 >> 2);
+    const int c = 4 * cb + 2 * (G & 1) + ((s16 >> 1) & 1);
+    return 128u * tl + 16u * (c ^ swz(tl)) + 8u * (s16 & 1);
+  };
+
+  // ---- copies: wave w moves 1 KB blocks p = 9 w .. 9 w + 8 of a chunk, block
+  // p = (column block q = p >> 2, token octet r = p & 3); lane l fetches token
+  // 8 r + (l >> 3), the 16-byte chunk that lands at its LDS position.  The
+  // lane's source offset depends on r only through r & 1 (the swizzle) and
+  // 8 r rows + 128 q bytes, which go in the scalar offset.
+  struct CopySrc {
+    __amdgpu_buffer_rsrc_t rsrc;
+    uint32_t lane_off;  // for even r; odd r swaps 32-byte halves (swz flips bit 1)
+    bool on;
+  };
+  auto copy_src = [&](const Chunk& c) -> CopySrc {
+    CopySrc cs;
+    cs.on = c.valid() && c.tok > 0;
+    cs.rsrc = chunk_rsrc(a, c);
+    const int ln = opaque(lane);  // rebuilt per chunk: held, the offsets would cost VGPRs across the loop
+    const int l3 = ln >> 3, l7 = ln & 7;
+    cs.lane_off = (uint32_t)l3 * row_bytes + 16u * (uint32_t)(l7 ^ swz(l3));
+    return cs;
+  };
+  auto copy_one = [&](const CopySrc& cs, uint32_t slot_addr, auto ic) {
+    constexpr int i = decltype(ic)::value;
+    const int p = 9 * w + i;
+    const int q = p >> 2, r = p & 3;
+    // row_bytes is a multiple of 128, so for odd r the swizzle's flipped bit 1
+    // is bit 5 of the offset.  (The whole offset goes in the VGPR: the scalar
+    // offset of an LDS-direct load does not address the source the same way.)
+    const uint32_t lo = (r & 1) ? (cs.lane_off ^ 32u) : cs.lane_off;
+    lds_dma16(cs.rsrc, lo + (8u * (uint32_t)r * row_bytes + 128u * (uint32_t)q), slot_addr + 4096u * q + 1024u * r);
+  };
+  auto copy_chunk = [&](const Chunk& c, uint32_t slot_addr) -> bool {
+    const CopySrc cs = copy_src(c);
+    if (!cs.on) return false;
+    static_for<0, kCopiesW>([&](auto ic) { copy_one(cs, slot_addr, ic); });
+    return true;
+  };
+
+  // ---- state
+  bf16x8 qf[kSSteps];          // queries of the segment being scored
+  f32x16 s;                    // scores of the chunk being scored
+  acc_zero();                  // output rows (the accumulator AGPRs)
+  // P^T of chunk t (the value product's B operand); the softmax of chunk t + 1
+  // overwrites each half after the value product's last use of it
+  bf16x8 pc[2];
+  pc[0] = pc[1] = bf16x8{};
+  float m_ref = -INFINITY;     // reference max of this lane's row (log2 units)
+  float lsum = 0.f;            // running sum of 2^(x - m_ref) over this lane's tokens
+  int lim = 0, lim_min = 0;    // visible keys of this row / smallest of the wave
+  float pend_f = 1.f;          // pending rescale of o (the reference moved)
+  bool pending = false;
+  float cap_inv = 0.f, cap_lse = -INFINITY;  // results of the last segment scored
+  float seg_inv = 0.f, seg_lse = -INFINITY;  // ... of the segment being accumulated
   bool seg_bad = false;
   int seg_slot = 0, seg_nsplit = 1;
 
-  // Queries of this wave's rows for the segment of chunk c, and the
-  // visible-key limits.  Waits for the loads here, before the next copy is
-  // issued, so that no later wait for them also waits for that copy.
-  auto load_queries = [&](const Chunk& c, int g, int r16) {
+  auto load_queries = [&](const Chunk& c) {
     const int n = clamp_len(a, load_len(a, c.seq));
+    const RowInfo ri = row_info();
+    const uint16_t* qp =
+        a.q + (int64_t)c.seq * a.q_sb + (int64_t)ri.qi * a.q_ss + (int64_t)ri.hh * a.q_sh + 8 * hlf;
 #pragma unroll
-    for (int rl = 0; rl < 2; ++rl) {
-      const int row = pi.blk_row0 + 32 * w + 16 * rl + r16;
-      const bool ok = row < a.rows;
-      const int rr = ok ? row : 0;  // rows past the last one score row 0's query, all masked
-      const int qi = rr / a.h_q, h = rr - qi * a.h_q;
-      const uint16_t* qp = a.q + (int64_t)c.seq * a.q_sb + (int64_t)qi * a.q_ss + (int64_t)h * a.q_sh + 8 * g;
+    for (int ks = 0; ks < kSSteps; ++ks) qf[ks] = *(const bf16x8*)(qp + 16 * ks);
+    lim = ri.ok ? (a.causal ? n - (a.s_q - 1 - ri.qi) : n) : 0;
+    lim_min = wave_full ? (a.causal ? n - (a.s_q - 1 - qi_min) : n) : 0;
+    m_ref = -INFINITY;
+    lsum = 0.f;
+  };
+  // The query loads have landed: waits for them here (and for the older chunk
+  // copies, which must land in this step anyway) and hands the registers on as
+  // new values, so that no later wait for them also waits for copies issued
+  // after this point.
+  auto queries_ready = [&]() {
 #pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) qf[rl][ks] = *(const bf16x8*)(qp + 32 * ks);
-    }
-    // chunks below every row's limit need no masking; a wave with rows past
-    // the last one masks every chunk
-    lim_min = pi.blk_row0 + 32 * w + 32 > a.rows ? 0 : (a.causal ? n - (a.s_q - 1) : n);
-    seg_n = n;
-    // waits here for the loads; the queries stay in VGPRs (the accumulators fill the AGPRs)
-#pragma unroll
-    for (int rl = 0; rl < 2; ++rl)
-#pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) asm volatile("" : "+v"(qf[rl][ks]));
+    for (int ks = 0; ks < kSSteps; ++ks) asm volatile("" : "+v"(qf[ks]));
   };
 
-  // ---- prologue: the first descriptor batch; copies of chunks 0 and 1;
+  // ---- the score product of chunk c (in the slot at byte offset slot_off),
+  // with the copies [C0, C1) of chunk cc issued between the MFMAs
+  auto score_loop = [&](uint32_t slot_off, auto with_copies, const Chunk& cc, uint32_t cc_slot, bool& issued) {
+    constexpr bool WC = decltype(with_copies)::value;
+    lds_u8* kb[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) kb[u] = launder(lds + slot_off + koff(opaque(lane), u));
+    auto kfrag = [&](int ks) -> bf16x8 { return *(const lds_bf16x8*)(kb[ks & 3] + 4096u * (ks >> 2)); };
+    bf16x8 kf[kKAhead + 1];
+#pragma unroll
+    for (int ks = 0; ks < kKAhead; ++ks) kf[ks] = kfrag(ks);
+    CopySrc cs;
+    if constexpr (WC) cs = copy_src(cc);
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, kSSteps>([&](auto kc) {
+      constexpr int ks = decltype(kc)::value;
+      constexpr int R = kKAhead + 1;
+      if constexpr (ks + kKAhead < kSSteps) kf[(ks + kKAhead) % R] = kfrag(ks + kKAhead);
+      score_mfma(s, kf[ks % R], qf[ks], ks == 0);
+      if constexpr (WC && ks % 4 == 1 && ks / 4 < kCopiesW) {
+        if (cs.on) copy_one(cs, cc_slot, std::integral_constant<int, ks / 4>{});
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if constexpr (WC) issued = cs.on;
+  };
+
+  // ---- softmax of the scored chunk D (scores in s), in 32 pieces; piece q
+  // runs after value MFMA q when interleaved
+  float mu = 0.f;
+  auto smax_piece = [&](auto qc, const Chunk& D) {
+    constexpr int q = decltype(qc)::value;
+    if constexpr (q == 0) {
+      mfma_result_wait();
+      mu = m_ref == -INFINITY ? 0.f : m_ref;
+    } else if constexpr (q >= 1 && q <= 4) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[4 * (q - 1) + e] = __builtin_fmaf(s[4 * (q - 1) + e], sc, -mu);
+    } else if constexpr (q == 5) {
+      // keys past the row's limit (only chunks that reach the smallest limit)
+      const int tok0 = kChunk * D.chunk;
+      if (D.tok <= 0 || tok0 + kChunk > lim_min) {
+        const int vis = (D.tok > 0 ? lim - tok0 : 0) - 4 * hlf;  // token 8 g + 4 hlf + e visible iff 8 g + e < vis
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (8 * (i >> 2) + (i & 3) >= vis) s[i] = -INFINITY;
+      }
+    } else if constexpr (q == 6) {
+      // the lane's chunk max (kept in pend_f's neighbour below)
+    } else if constexpr (q == 7) {
+      float mx = s[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+      const bool over = m_ref == -INFINITY ? mx > -INFINITY : mx > kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(over) != 0) {
+        // a chunk max passed the reference by more than 2^16 (or the segment
+        // just started): move the row's reference to its max
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(mx), __float_as_int(mx), false, false);
+        const float rowmax = fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1])) + mu;
+        const float m_new = fmaxf(m_ref, rowmax);
+        const float f = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+        const float mu_new = m_new == -INFINITY ? 0.f : m_new;
+        lsum *= f;
+        m_ref = m_new;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] += mu - mu_new;
+        mu = mu_new;
+        if (!D.first) {
+          pend_f = f;
+          pending = true;
+        }
+      }
+    } else if constexpr (q >= 8 && q < 24) {
+      s[q - 8] = __builtin_amdgcn_exp2f(s[q - 8]);
+    } else if constexpr (q >= 24 && q < 28) {
+      const int i = 4 * (q - 24);
+      lsum += (s[i] + s[i + 1]) + (s[i + 2] + s[i + 3]);
+    } else if constexpr (q == 28 || q == 31) {
+      // P^T half kk (value MFMAs 16 kk .. 16 kk + 15 are issued by now; the
+      // last one reads the registers this overwrites, so wait a few cycles)
+      const int kk = q == 28 ? 0 : 1;
+      if constexpr (q == 31) {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_nop 7" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      bf16x8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (__bf16)s[8 * kk + e];
+      pc[kk] = v;
+    } else if constexpr (q == 30) {
+      if (D.last) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(lsum), __float_as_int(lsum), false, false);
+        const float l = __int_as_float(sw[0]) + __int_as_float(sw[1]);
+        cap_inv = l > 0.f ? 1.f / l : 0.f;
+        cap_lse = l > 0.f ? (m_ref + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
+      }
+    }
+  };
+
+  // ---- the value product of chunk t (slot at slot_off), optionally with the
+  // softmax of chunk D between its MFMAs
+  auto value_loop = [&](uint32_t slot_off, auto with_smax, const Chunk& D) {
+    constexpr bool WS = decltype(with_smax)::value;
+    lds_u8* vb[2][2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) vb[cb][b] = launder(lds + slot_off + voff(opaque(lane), cb, b));
+    auto vfrag = [&](int f) -> bf16x8 {
+      const int kk = f >> 4, ct = f & 15;
+      const uint32_t off = 4096u * (ct >> 1) + 2048u * kk;
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb[ct & 1][0] + off));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb[ct & 1][1] + off));
+      return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    bf16x8 vf[kVAhead + 1];
+#pragma unroll
+    for (int f = 0; f < kVAhead; ++f) vf[f] = vfrag(f);
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, 2 * kColTiles>([&](auto fc) {
+      constexpr int f = decltype(fc)::value;
+      constexpr int R = kVAhead + 1;
+      if constexpr (f + kVAhead < 2 * kColTiles) vf[(f + kVAhead) % R] = vfrag(f + kVAhead);
+      value_mfma<(f & 15)>(vf[f % R], pc[f >> 4]);
+      if constexpr (WS) smax_piece(fc, D);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  // ---- the end of chunk D0's segment: this wave's rows of out (or of the
+  // split's fp32 partial) and lse; then clear the accumulators
+  auto segment_end = [&](const Chunk& D0) {
+    float inv = seg_inv, lse = seg_lse;
+    if (seg_bad) {
+      inv = __builtin_nanf("");
+      lse = __builtin_nanf("");
+    }
+    mfma_result_wait();
+    const RowInfo ri = row_info();
+    const int row = ri.row;
+    if (ri.ok) {
+      const int col0 = 4 * hlf;
+      if (seg_nsplit == 1) {
+        uint16_t* op =
+            a.out + (int64_t)D0.seq * a.o_sb + (int64_t)ri.qi * a.o_ss + (int64_t)ri.hh * a.o_sh + col0;
+        static_for<0, 4 * kColTiles>([&](auto ic) {
+          constexpr int I = decltype(ic)::value;  // tile I >> 2, elements 4 (I & 3) ..
+          const f32x4 v = acc_read4<I>() * inv;
+          *(bf16x4*)(op + 32 * (I >> 2) + 8 * (I & 3)) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+        });
+        if (hlf == 0) a.lse[(int64_t)D0.seq * a.l_sb + (int64_t)ri.qi * a.l_ss + (int64_t)ri.hh * a.l_sh] = lse;
+      } else {
+        float* pp = a.part_o + ((int64_t)seg_slot * a.rows + row) * kDv + col0;
+        static_for<0, 4 * kColTiles>([&](auto ic) {
+          constexpr int I = decltype(ic)::value;
+          *(f32x4*)(pp + 32 * (I >> 2) + 8 * (I & 3)) = acc_read4<I>() * inv;
+        });
+        if (hlf == 0) a.part_lse[(int64_t)seg_slot * a.rows + row] = lse;
+      }
+    }
+    acc_zero();
+    asm volatile("s_nop 4" ::: "memory");
+  };
+
+  // ---- prologue: the first descriptor batch, copies of chunks 0 and 1, the
   // queries of the first segment
   BatchPos bpos;
   bpos.seq = pi.seq_begin;
@@ -371,50 +646,23 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
   Chunk D1 = batch_get(batch, 0);                // chunk t + 1: scores
   Chunk D2 = batch_get(batch, 1);                // chunk t + 2: landing
   Chunk D3 = batch_get(batch, 2);                // chunk t + 3: copied this step
-  {
-    const LaneMap lm(lane, w, row_bytes);
-    wide_copy(a, D1, lds_addr, lds_addr + kRopeOff, w, lm.cp0, lm.cp1);
-    wide_copy(a, D2, lds_addr + kLatBytes, lds_addr + kRopeOff + kRopeBytes, w, lm.cp0, lm.cp1);
-    if (D1.valid()) load_queries(D1, lm.g, lm.r16);
-  }
+  copy_chunk(D1, lds_addr);
+  copy_chunk(D2, lds_addr + kTileBytes);
+  if (D1.valid()) load_queries(D1);
+  queries_ready();
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  int rs1 = 0;    // rope slot of chunk t + 1 (chunk ordinal mod 3)
-  int s_seg = 0;  // segments whose results the score side has published
-  int v_seg = 0;  // segments the value side has closed
 
   for (int t = -1;; ++t) {
     if (!D0.valid() && !D1.valid()) break;
-    const int par = t & 1, par1 = (t + 1) & 1;
     const bool v_has = D0.valid() && D0.tok > 0;
     const bool s_has = D1.valid() && D1.tok > 0;
-    bool drain = false;  // this step issued other vector memory work: wait for all of it
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const int g = ln >> 4, r16 = ln & 15;
+    const uint32_t slot0 = (uint32_t)(t & 3) * kTileBytes;
+    const uint32_t slot1 = (uint32_t)((t + 1) & 3) * kTileBytes;
+    const uint32_t slot3 = lds_addr + (uint32_t)((t + 3) & 3) * kTileBytes;
+    bool issued = false;
 
-    // ---- chunk t + 1 starts a segment: its queries (the first ones were
-    // loaded in the prologue) and a fresh softmax state
-    if (D1.valid() && D1.first) {
-      if (t >= 0) {
-        load_queries(D1, g, r16);
-        drain = true;
-      }
-#pragma unroll
-      for (int rl = 0; rl < 2; ++rl) {
-        m_ref[rl] = -INFINITY;
-        lsum[rl] = 0.f;
-      }
-    }
-    // ---- copy chunk t + 3 into the slots of chunks t - 1 (latent) and t (rope)
-    const int rs3 = rs1 == 0 ? 2 : rs1 - 1;
-    bool issued;
-    {
-      const LaneMap lm(fresh_lane(lane), w, row_bytes);
-      issued = wide_copy(a, D3, lds_addr + (uint32_t)((t + 3) & 3) * kLatBytes,
-                         lds_addr + kRopeOff + (uint32_t)rs3 * kRopeBytes, w, lm.cp0, lm.cp1);
-    }
-    // ---- the values enter a new segment
+    // the values enter a new segment / close one
     if (D0.valid() && D0.first) {
       const int split = D0.seq == pi.seq_begin ? pi.split_first : 0;
       const int s0 = ((cint32*)a.num_splits)[D0.seq];
@@ -422,248 +670,51 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
       seg_nsplit = ((cint32*)a.num_splits)[D0.seq + 1] - s0;
       seg_bad = false;
     }
-    if (D0.valid()) seg_bad |= D0.bad;
-
-    // ---- scores of chunk t + 1: 32 rows x 32 tokens, two MFMAs per K read
-    f32x4 s[2][2] = {};  // [token tile][row tile]
-    if (s_has) {
-      const LaneMap lm(fresh_lane(lane), w, row_bytes);
-      lds_u8* const lat = lds + (uint32_t)((t + 1) & 3) * kLatBytes;
-      lds_u8* const rope = lds + kRopeOff + (uint32_t)rs1 * kRopeBytes;
-      lds_u8* const kb0 = launder(lat + lm.k_lat + 16u * lm.kx);
-      lds_u8* const kb1 = launder(lat + lm.k_lat + 16u * (lm.kx ^ 4u));
-      lds_u8* const rb0 = launder(rope + lm.k_rope + 16u * lm.kx);
-      lds_u8* const rb1 = launder(rope + lm.k_rope + 16u * (lm.kx ^ 4u));
-      auto kfrag = [&](int ks, int tt) -> bf16x8 {
-        if (ks < 16) return *(const lds_bf16x8*)(((ks & 1) ? kb1 : kb0) + 16384u * tt + 1024u * (ks >> 1));
-        return *(const lds_bf16x8*)(((ks & 1) ? rb1 : rb0) + 2048u * tt);
-      };
-      // K fragments in flight: a ring of kKAheadW + 1 pairs
-      bf16x8 kf[kKAheadW + 1][2];
-#pragma unroll
-      for (int ks = 0; ks < kKAheadW; ++ks) {
-        kf[ks][0] = kfrag(ks, 0);
-        kf[ks][1] = kfrag(ks, 1);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) {
-        constexpr int R = kKAheadW + 1;
-        if (ks + kKAheadW < kKSteps) {
-          kf[(ks + kKAheadW) % R][0] = kfrag(ks + kKAheadW, 0);
-          kf[(ks + kKAheadW) % R][1] = kfrag(ks + kKAheadW, 1);
-        }
-        score_mfma(s, kf[ks % R][0], kf[ks % R][1], qf[0][ks], qf[1][ks], ks == 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // without a value product behind it, the softmax would read the scores
-      // right away
-      if (!v_has) score_done(s);
-    }
-    section_fence();
-
-    // ---- rows whose reference moved at chunk t: rescale what they have
-    // accumulated so far
-    const i32x4 fl = *(const lds_i32x4*)(flags + 4 * par);
-    if (v_has && uniform(fl[0] | fl[1] | fl[2] | fl[3])) {
-      const lds_f32* fp = fac + par * kRowsW + r16;
-#pragma unroll
-      for (int rt = 0; rt < kRowTiles; ++rt) {
-        if (uniform(fl[rt >> 1])) {
-          const float f = fp[16 * rt];
-          acc_ready(o[rt]);
-#pragma unroll
-          for (int ct = 0; ct < 8; ++ct) o[rt][ct] *= f;
-        }
+    if (D0.valid()) {
+      seg_bad |= D0.bad;
+      if (D0.last) {
+        seg_inv = cap_inv;
+        seg_lse = cap_lse;
       }
     }
-
-    section_fence();
-    // ---- values of chunk t, O^T[columns 128 w ..] += V^T . P^T, in 16 groups
-    // of four MFMAs; the softmax of chunk t + 1 runs in the VALU between them
-    lds_u8* vb[4];
-    lds_u8* pp;
-    bf16x8 pf[4];  // P^T fragments of four row tiles (the first, then the second half)
-    bf16x8 vr[3];  // V^T fragments in flight: group k uses vr[k % 3], read two groups ahead
-    auto vfrag = [&](int ct) -> bf16x8 {
-      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb[ct & 3] + 1024u * (ct >> 2)));
-      const bf16x4 hi =
-          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb[ct & 3] + 1024u * (ct >> 2) + 16384u));
-      return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    };
-    auto v_setup = [&]() {
-      const LaneMap lm(fresh_lane(lane), w, row_bytes);
-      lds_u8* const lat = lds + (uint32_t)(t & 3) * kLatBytes;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) vb[u] = launder(lat + lm.v_lane + 16u * ((2u * u) ^ lm.vy));
-      pp = lds + kPOff + 16u * fresh_lane(lane) + (uint32_t)par * (kRowTiles * 1024);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pf[i] = *(const lds_bf16x8*)(pp + 1024u * i);
-      vr[0] = vfrag(0);
-      vr[1] = vfrag(1);
-    };
-    // softmax state of this step (lane holds tokens 32 chunk + 16 tt + 4 g + j
-    // of row 16 rl + r16, as x[rl][4 tt + j], in log2 units less mu[rl])
-    float x[2][8];
-    float mu[2], mx[2];
-    bf16x8 pv[2];
-    bool moved = false;
-    // 64 single MFMAs (row tiles 0..3 over the eight column tiles, then 4..7:
-    // V read twice, half of P held); group q works on column tile (q >> 2) & 7,
-    // row tile 4 (q >> 5) + (q & 3)
-    auto v_group = [&](auto qc) {
-      constexpr int q = decltype(qc)::value;
-      const int cg = q >> 2, ct = cg & 7, i = q & 3, half = q >> 5;
-      if constexpr (i == 0 && cg + 2 < 16) vr[(cg + 2) % 3] = vfrag((cg + 2) & 7);
-      value_mfma1(o[4 * half + i][ct], vr[cg % 3], pf[i], i == 0);
-      // the second half's P fragments, each right after its last use
-      if constexpr (half == 0 && ct == 7) pf[i] = *(const lds_bf16x8*)(pp + 1024u * (4 + i));
-    };
-    // the softmax of chunk t + 1 in small pieces, one after each MFMA
-    auto s_piece = [&](auto qc) {
-      constexpr int q = decltype(qc)::value;
-      if constexpr (q >= 4 && q < 8) {
-        const int rl = (q - 4) >> 1, tt = (q - 4) & 1;
-        if (tt == 0) mu[rl] = m_ref[rl] == -INFINITY ? 0.f : m_ref[rl];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x[rl][4 * tt + j] = __builtin_fmaf(s[tt][rl][j], sc, -mu[rl]);
-      } else if constexpr (q == 8) {
-        // mask keys past each row's limit (only chunks that reach a limit)
-        const int tok0 = kChunk * D1.chunk;
-        if (!s_has || tok0 + kChunk > lim_min) {
-#pragma unroll
-          for (int rl = 0; rl < 2; ++rl) {
-            // the row's visible-key limit (rows past the last one see nothing)
-            const int row = pi.blk_row0 + 32 * w + 16 * rl + r16;
-            const int qi = row / a.h_q;
-            const int lim = row < a.rows ? seg_n - (a.causal ? a.s_q - 1 - qi : 0) : 0;
-            const int vis = s_has ? lim - tok0 - 4 * g : 0;
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-              for (int j = 0; j < 4; ++j)
-                if (16 * tt + j >= vis) x[rl][4 * tt + j] = -INFINITY;
-          }
-        }
-      } else if constexpr (q == 9 || q == 10) {
-        const int rl = q - 9;
-        mx[rl] = fmaxf(fmaxf(fmaxf(x[rl][0], x[rl][1]), fmaxf(x[rl][2], x[rl][3])),
-                       fmaxf(fmaxf(x[rl][4], x[rl][5]), fmaxf(x[rl][6], x[rl][7])));
-      } else if constexpr (q == 11) {
-        bool over = false;
-#pragma unroll
-        for (int rl = 0; rl < 2; ++rl)
-          over |= m_ref[rl] == -INFINITY ? mx[rl] > -INFINITY : mx[rl] > kRescaleSlack;
-        moved = __builtin_amdgcn_ballot_w64(over) != 0;
-        if (moved) {
-          // a chunk max passed the reference by more than 2^16 (or the
-          // segment just started): move every row's reference to its max
-#pragma unroll
-          for (int rl = 0; rl < 2; ++rl) {
-            const float rowmax = wave_max16(mx[rl]) + mu[rl];
-            const float m_new = fmaxf(m_ref[rl], rowmax);
-            const float f = m_ref[rl] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref[rl] - m_new);
-            const float mu_new = m_new == -INFINITY ? 0.f : m_new;
-            lsum[rl] *= f;
-            m_ref[rl] = m_new;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) x[rl][i] += mu[rl] - mu_new;
-            mu[rl] = mu_new;
-            if (g == 0) fac[par1 * kRowsW + 32 * w + 16 * rl + r16] = f;
-          }
-        }
-      } else if constexpr (q >= 12 && q < 28) {
-        const int rl = (q - 12) >> 3, i = (q - 12) & 7;
-        x[rl][i] = __builtin_amdgcn_exp2f(x[rl][i]);
-      } else if constexpr (q >= 28 && q < 36) {
-        const int rl = (q - 28) >> 2, i = 2 * ((q - 28) & 3);
-        lsum[rl] += x[rl][i] + x[rl][i + 1];
-      } else if constexpr (q >= 36 && q < 44) {
-        const int rl = (q - 36) >> 2, i = 2 * ((q - 36) & 3);
-        pv[rl][i] = (__bf16)x[rl][i];
-        pv[rl][i + 1] = (__bf16)x[rl][i + 1];
-      } else if constexpr (q == 44 || q == 45) {
-        const int rl = q - 44;
-        *(lds_bf16x8*)(lds + kPOff + 16u * fresh_lane(lane) + par1 * (kRowTiles * 1024) + 1024u * (2 * w + rl)) =
-            pv[rl];
-        if (rl == 1 && lane == 0) flags[4 * par1 + w] = moved ? 1 : 0;
+    // the reference max of some rows moved at chunk t: rescale their sums
+    if (pending) {
+      if (v_has) {
+        mfma_result_wait();
+        acc_scale(pend_f);
+        asm volatile("s_nop 4" ::: "memory");
       }
-    };
-    // (a chunk without keys runs the softmax fully masked: no state changes,
-    // P = 0)
-    if (v_has) {
-      v_setup();
-      __builtin_amdgcn_sched_barrier(0);
-      static_for<0, 64>([&](auto qc) {
-        v_group(qc);
-        s_piece(qc);
-        __builtin_amdgcn_sched_barrier(0);
-      });
+      pending = false;
+      pend_f = 1.f;
+    }
+
+    if (D1.valid() && D1.first && t >= 0) {
+      // ---- a new segment is scored: queries first, values of chunk t, the
+      // end of its segment, then the scores and the softmax
+      load_queries(D1);
+      if (v_has) value_loop(slot0, std::false_type{}, D1);
+      if (D0.valid() && D0.last) segment_end(D0);
+      queries_ready();
+      if (s_has) score_loop(slot1, std::false_type{}, D3, slot3, issued);
+      static_for<0, 2 * kColTiles>([&](auto qc) { smax_piece(qc, D1); });
+      issued = copy_chunk(D3, slot3);
     } else {
-      static_for<0, 64>([&](auto qc) { s_piece(qc); });
-    }
-    // ---- chunk t + 1 ends its segment: publish 1 / (sum of p) and lse of the rows
-    if (D1.valid() && D1.last) {
-      lds_f32* const fs = fin + (s_seg & 1) * (2 * kRowsW);
-#pragma unroll
-      for (int rl = 0; rl < 2; ++rl) {
-        const float l = wave_sum16(lsum[rl]);
-        const float inv = l > 0.f ? 1.f / l : 0.f;
-        const float lse = l > 0.f ? (m_ref[rl] + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
-        if (g == 0) {
-          fs[32 * w + 16 * rl + r16] = inv;
-          fs[kRowsW + 32 * w + 16 * rl + r16] = lse;
-        }
+      if (s_has) {
+        score_loop(slot1, std::true_type{}, D3, slot3, issued);
+      } else {
+        issued = copy_chunk(D3, slot3);
       }
-      ++s_seg;
-    }
-
-    // ---- chunk t ends its segment: write this wave's columns of every row
-    if (D0.valid() && D0.last) {
-      const lds_f32* const fs = fin + (v_seg & 1) * (2 * kRowsW) + r16;
-      const bool final_out = seg_nsplit == 1;
-      int row0 = pi.blk_row0 + r16;  // opaque: keeps the address arithmetic in this block
-      asm volatile("" : "+v"(row0));
-#pragma unroll
-      for (int rt = 0; rt < kRowTiles; ++rt) {
-        float inv = fs[16 * rt];
-        float lse = fs[kRowsW + 16 * rt];
-        acc_ready(o[rt]);
-        if (seg_bad) {
-          inv = __builtin_nanf("");
-          lse = __builtin_nanf("");
-        }
-        const int row = row0 + 16 * rt;
-        if (row < a.rows) {
-          const int qi = row / a.h_q, h = row - qi * a.h_q;
-          const int col0 = 128 * w + 4 * g;
-          if (final_out) {
-            uint16_t* op = a.out + (int64_t)D0.seq * a.o_sb + (int64_t)qi * a.o_ss + (int64_t)h * a.o_sh + col0;
-#pragma unroll
-            for (int ct = 0; ct < 8; ++ct) {
-              const f32x4 v = o[rt][ct] * inv;
-              *(bf16x4*)(op + 16 * ct) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-            }
-            if (w == 0 && g == 0)
-              a.lse[(int64_t)D0.seq * a.l_sb + (int64_t)qi * a.l_ss + (int64_t)h * a.l_sh] = lse;
-          } else {
-            float* pp = a.part_o + ((int64_t)seg_slot * a.rows + row) * kDv + col0;
-#pragma unroll
-            for (int ct = 0; ct < 8; ++ct) *(f32x4*)(pp + 16 * ct) = o[rt][ct] * inv;
-            if (w == 0 && g == 0) a.part_lse[(int64_t)seg_slot * a.rows + row] = lse;
-          }
-        }
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct) o[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-      ++v_seg;
-      drain = true;
+      if (v_has)
+        value_loop(slot0, std::true_type{}, D1);
+      else if (D1.valid())
+        static_for<0, 2 * kColTiles>([&](auto qc) { smax_piece(qc, D1); });
+      if (D0.valid() && D0.last) segment_end(D0);
     }
 
     // ---- end of step: this wave's share of chunk t + 2 has landed (that of
-    // chunk t + 3 may still be in flight); all LDS reads have returned
-    static_assert(kCopyLoadsW == 9, "vmcnt below");
-    if (issued && !drain)
+    // chunk t + 3, the last vector memory loads issued, may still be in flight)
+    static_assert(kCopiesW == 9, "vmcnt below");
+    if (issued)
       asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -677,7 +728,6 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
       c0 += 64;
     }
     D3 = batch_get(batch, t + 4 - c0);
-    rs1 = rs1 == 2 ? 0 : rs1 + 1;
   }
 }
 
