@@ -56,7 +56,7 @@ constexpr int kSmemW = kSlots * kTileBytes;       // 147456
 constexpr int kSSteps = kD / 16;                  // 36 score k-steps
 constexpr int kColTiles = kDv / 32;               // 16 output column tiles
 constexpr int kCopiesW = 9;                       // 1 KB copies per wave per chunk
-constexpr int kKAhead = 7;                        // score K fragments in flight
+constexpr int kKAhead = 6;                        // score K fragments in flight
 constexpr int kVAhead = 6;                        // value V^T fragments in flight
 static_assert(kSmemW <= 160 * 1024, "LDS budget");
 static_assert(kThreadsW / 64 * kCopiesW * 1024 == kTileBytes, "copies cover the chunk");
@@ -66,6 +66,16 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // Swizzle of token a's eight 16-byte chunks in a column block (uses bits 1..3
 // of a, so it repeats every 16 tokens).
 __device__ __forceinline__ int swz(int a) { return (((a >> 1) & 1) << 2) | ((a >> 2) & 3); }
+
+// Column block Q (1 KB) of the wave's token octet: source at lane_off + 128 Q
+// (the immediate offset), LDS at wave_base + 4096 Q (the immediate offset is
+// added to the LDS address too, so M0 is lowered by it).
+template <int Q>
+__device__ __forceinline__ void copy_block(__amdgpu_buffer_rsrc_t rsrc, uint32_t lane_off, uint32_t wave_base) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen offset:%2 lds" ::"v"(lane_off), "s"(rsrc), "n"(128 * Q),
+               "{m0}"(wave_base + (4096u - 128u) * Q)
+               : "memory");
+}
 
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -80,46 +90,44 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
-// s (+)= K . Q^T for one 16-column step of d; the accumulator stays in VGPRs
+// s (+)= K . Q^T for two 16-column steps of d; the accumulator stays in VGPRs
 // (written as assembly: the compiler would put every MFMA result of the
-// kernel in the register file the value accumulators fill).  The compiler
-// does not see an MFMA here, so the two wait states an operand written by a
-// VALU move needs are part of it.
-__device__ __forceinline__ void score_mfma(f32x16& s, bf16x8 k, bf16x8 q, bool first) {
+// kernel in the register file the value accumulators fill).  Two MFMAs per
+// statement: one wait for the operands of both.
+__device__ __forceinline__ void score_mfma2(f32x16& s, bf16x8 k0, bf16x8 k1, bf16x8 q0, bf16x8 q1, bool first) {
   if (first)
-    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(k), "v"(q));
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %3, 0\n\tv_mfma_f32_32x32x16_bf16 %0, %2, %4, %0"
+        : "=&v"(s)
+        : "v"(k0), "v"(k1), "v"(q0), "v"(q1));
   else
-    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(k), "v"(q));
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %3, %0\n\tv_mfma_f32_32x32x16_bf16 %0, %2, %4, %0"
+        : "+v"(s)
+        : "v"(k0), "v"(k1), "v"(q0), "v"(q1));
 }
 
 // ---- the output accumulators: fixed AGPRs, a[16 ct .. 16 ct + 15] for tile
 // ct, touched only by the assembly below (the compiler never holds them, so
 // it cannot copy or spill them; the zeroing names every one of them as
 // clobbered, which reserves all 256 for the kernel).
-// (the compiler does not see these as MFMAs: the two wait states cover an
-// operand it may have just assembled with VALU moves)
-#define MLA_VMFMA(LO, HI) \
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 a[" #LO ":" #HI "], %0, %1, a[" #LO ":" #HI "]" ::"v"(v), "v"(p))
+// Two value MFMAs, tiles CT and CT + 1 (CT even), in one statement: one wait
+// for both operands.
+#define MLA_VMFMA2(L0, H0, L1, H1)                                                                  \
+  asm volatile("v_mfma_f32_32x32x16_bf16 a[" #L0 ":" #H0 "], %0, %2, a[" #L0 ":" #H0 "]\n\t"           \
+               "v_mfma_f32_32x32x16_bf16 a[" #L1 ":" #H1 "], %1, %2, a[" #L1 ":" #H1 "]" ::"v"(v0), \
+               "v"(v1), "v"(p))
 template <int CT>
-__device__ __forceinline__ void value_mfma(bf16x8 v, bf16x8 p) {
-  if constexpr (CT == 0) MLA_VMFMA(0, 15);
-  else if constexpr (CT == 1) MLA_VMFMA(16, 31);
-  else if constexpr (CT == 2) MLA_VMFMA(32, 47);
-  else if constexpr (CT == 3) MLA_VMFMA(48, 63);
-  else if constexpr (CT == 4) MLA_VMFMA(64, 79);
-  else if constexpr (CT == 5) MLA_VMFMA(80, 95);
-  else if constexpr (CT == 6) MLA_VMFMA(96, 111);
-  else if constexpr (CT == 7) MLA_VMFMA(112, 127);
-  else if constexpr (CT == 8) MLA_VMFMA(128, 143);
-  else if constexpr (CT == 9) MLA_VMFMA(144, 159);
-  else if constexpr (CT == 10) MLA_VMFMA(160, 175);
-  else if constexpr (CT == 11) MLA_VMFMA(176, 191);
-  else if constexpr (CT == 12) MLA_VMFMA(192, 207);
-  else if constexpr (CT == 13) MLA_VMFMA(208, 223);
-  else if constexpr (CT == 14) MLA_VMFMA(224, 239);
-  else if constexpr (CT == 15) MLA_VMFMA(240, 255);
+__device__ __forceinline__ void value_mfma2(bf16x8 v0, bf16x8 v1, bf16x8 p) {
+  static_assert(CT % 2 == 0 && CT < 16, "tile pair");
+  if constexpr (CT == 0) MLA_VMFMA2(0, 15, 16, 31);
+  else if constexpr (CT == 2) MLA_VMFMA2(32, 47, 48, 63);
+  else if constexpr (CT == 4) MLA_VMFMA2(64, 79, 80, 95);
+  else if constexpr (CT == 6) MLA_VMFMA2(96, 111, 112, 127);
+  else if constexpr (CT == 8) MLA_VMFMA2(128, 143, 144, 159);
+  else if constexpr (CT == 10) MLA_VMFMA2(160, 175, 176, 191);
+  else if constexpr (CT == 12) MLA_VMFMA2(192, 207, 208, 223);
+  else if constexpr (CT == 14) MLA_VMFMA2(224, 239, 240, 255);
 }
-#undef MLA_VMFMA
+#undef MLA_VMFMA2
 
 #define MLA_AREAD4(A, B, C, D)                                                                 \
   asm volatile("v_accvgpr_read_b32 %0, a" #A "\n\tv_accvgpr_read_b32 %1, a" #B                  \
@@ -378,56 +386,47 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
   const bool wave_full = pi.blk_row0 + 32 * w + 32 <= a.rows;
   const int qi_min = (pi.blk_row0 + 32 * w) / a.h_q;
 
-  // ---- per-lane LDS offsets inside a slot, recomputed where used from an
-  // opaque copy of the lane index (holding them would cost 8 VGPRs)
-  // score K fragment of k-step ks (u = ks & 3): token j32, 16-byte chunk 2 ks + hlf
-  auto koff = [](int ln, int u) -> uint32_t {
-    const int j = ln & 31, hb = ln >> 5;
-    return 128u * j + 16u * ((2 * u + hb) ^ swz(j));
-  };
-  // value V^T half fragment (ct & 1 = cb, b): 16-lane group G reads tokens
-  // 8 b + 4 (G >> 1) + 0..3 of the k-step, columns 16 (G & 1) + 0..15 of the tile
-  auto voff = [](int ln, int cb, int b) -> uint32_t {
-    const int G = ln >> 4, s16 = ln & 15;
-    const int tl = 8 * b + 4 * (G >> 1) + (s16 >> 2);
-    const int c = 4 * cb + 2 * (G & 1) + ((s16 >> 1) & 1);
-    return 128u * tl + 16u * (c ^ swz(tl)) + 8u * (s16 & 1);
-  };
+  // ---- per-lane LDS offsets inside a slot
+  // Score K fragment of k-step ks (u = ks & 3): token j of the lane's half,
+  // 16-byte chunk 2 ks + h at slot ((2 u + h) ^ swz(j)), i.e. at byte
+  // 128 j + 16 ((2 u + h) ^ swz(j)) = k_lane ^ 32 u of the column block (the u
+  // part only flips bits 5..6).
+  const uint32_t k_lane = [&] {
+    const int j = lane & 31, hb = lane >> 5, sw = swz(j);
+    return 128u * j + 16u * (uint32_t)(hb ^ (sw & 1)) + 32u * (uint32_t)(sw >> 1);
+  }();
+  // Value V^T half fragment (cb = ct & 1, b): 16-lane group G reads tokens
+  // 8 b + 4 (G >> 1) + 0..3 of the k-step, columns 16 (G & 1) + 0..15 of the
+  // tile, at v_lane ^ (64 cb + 32 b) + 1024 b (cb and b only flip bits 5..6 of
+  // the swizzled chunk; 1024 b is the token octet).
+  const uint32_t v_lane = [&] {
+    const int G = lane >> 4, s16 = lane & 15;
+    const int tl = 4 * (G >> 1) + (s16 >> 2);
+    const int c = 2 * (G & 1) + ((s16 >> 1) & 1);
+    return 128u * tl + 16u * (uint32_t)(c ^ swz(tl)) + 8u * (uint32_t)(s16 & 1);
+  }();
 
-  // ---- copies: wave w moves 1 KB blocks p = 9 w .. 9 w + 8 of a chunk, block
-  // p = (column block q = p >> 2, token octet r = p & 3); lane l fetches token
-  // 8 r + (l >> 3), the 16-byte chunk that lands at its LDS position.  The
-  // lane's source offset depends on r only through r & 1 (the swizzle) and
-  // 8 r rows + 128 q bytes, which go in the scalar offset.
-  struct CopySrc {
-    __amdgpu_buffer_rsrc_t rsrc;
-    uint32_t lane_off;  // for even r; odd r swaps 32-byte halves (swz flips bit 1)
-    bool on;
+  // ---- copies: wave w moves token octet w (tokens 8 w .. 8 w + 7) of the
+  // chunk's nine column blocks q, 1 KB each; lane l fetches token 8 w + (l >> 3)
+  // and the 16-byte chunk that lands at its LDS position.  A chunk without keys
+  // (or past the part's end) copies from an empty range: the loads write zeros
+  // and read nothing, and every step issues the same nine loads.  Column block
+  // q is the load's immediate offset 128 q, which an LDS-direct load also adds
+  // to its LDS address, so M0 is lowered by as much.
+  const uint32_t cp_lane = [&] {
+    const int tk = 8 * w + (lane >> 3);
+    return (uint32_t)tk * row_bytes + 16u * (uint32_t)((lane & 7) ^ swz(tk));
+  }();
+  auto copy_rsrc = [&](const Chunk& c) -> __amdgpu_buffer_rsrc_t {
+    const Chunk cz = c.valid() ? c : Chunk{0, 0, 0, 0, false, false, true};
+    return chunk_rsrc(a, cz);
   };
-  auto copy_src = [&](const Chunk& c) -> CopySrc {
-    CopySrc cs;
-    cs.on = c.valid() && c.tok > 0;
-    cs.rsrc = chunk_rsrc(a, c);
-    const int ln = opaque(lane);  // rebuilt per chunk: held, the offsets would cost VGPRs across the loop
-    const int l3 = ln >> 3, l7 = ln & 7;
-    cs.lane_off = (uint32_t)l3 * row_bytes + 16u * (uint32_t)(l7 ^ swz(l3));
-    return cs;
+  auto copy_one = [&](__amdgpu_buffer_rsrc_t rsrc, uint32_t slot_addr, auto qc) {
+    copy_block<decltype(qc)::value>(rsrc, cp_lane, slot_addr + 1024u * w);
   };
-  auto copy_one = [&](const CopySrc& cs, uint32_t slot_addr, auto ic) {
-    constexpr int i = decltype(ic)::value;
-    const int p = 9 * w + i;
-    const int q = p >> 2, r = p & 3;
-    // row_bytes is a multiple of 128, so for odd r the swizzle's flipped bit 1
-    // is bit 5 of the offset.  (The whole offset goes in the VGPR: the scalar
-    // offset of an LDS-direct load does not address the source the same way.)
-    const uint32_t lo = (r & 1) ? (cs.lane_off ^ 32u) : cs.lane_off;
-    lds_dma16(cs.rsrc, lo + (8u * (uint32_t)r * row_bytes + 128u * (uint32_t)q), slot_addr + 4096u * q + 1024u * r);
-  };
-  auto copy_chunk = [&](const Chunk& c, uint32_t slot_addr) -> bool {
-    const CopySrc cs = copy_src(c);
-    if (!cs.on) return false;
-    static_for<0, kCopiesW>([&](auto ic) { copy_one(cs, slot_addr, ic); });
-    return true;
+  auto copy_chunk = [&](const Chunk& c, uint32_t slot_addr) {
+    const __amdgpu_buffer_rsrc_t rsrc = copy_rsrc(c);
+    static_for<0, kCopiesW>([&](auto qc) { copy_one(rsrc, slot_addr, qc); });
   };
 
   // ---- state
@@ -471,29 +470,27 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
 
   // ---- the score product of chunk c (in the slot at byte offset slot_off),
   // with the copies [C0, C1) of chunk cc issued between the MFMAs
-  auto score_loop = [&](uint32_t slot_off, auto with_copies, const Chunk& cc, uint32_t cc_slot, bool& issued) {
+  auto score_loop = [&](uint32_t slot_off, auto with_copies, const Chunk& cc, uint32_t cc_slot) {
     constexpr bool WC = decltype(with_copies)::value;
     lds_u8* kb[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) kb[u] = launder(lds + slot_off + koff(opaque(lane), u));
+    for (int u = 0; u < 4; ++u) kb[u] = launder(lds + slot_off + (k_lane ^ (32u * u)));
     auto kfrag = [&](int ks) -> bf16x8 { return *(const lds_bf16x8*)(kb[ks & 3] + 4096u * (ks >> 2)); };
-    bf16x8 kf[kKAhead + 1];
+    constexpr int R = kKAhead + 2;  // the reads of a pair go ahead of the pair's MFMAs
+    bf16x8 kf[R];
 #pragma unroll
     for (int ks = 0; ks < kKAhead; ++ks) kf[ks] = kfrag(ks);
-    CopySrc cs;
-    if constexpr (WC) cs = copy_src(cc);
+    __amdgpu_buffer_rsrc_t rsrc;
+    if constexpr (WC) rsrc = copy_rsrc(cc);
     __builtin_amdgcn_sched_barrier(0);
-    static_for<0, kSSteps>([&](auto kc) {
-      constexpr int ks = decltype(kc)::value;
-      constexpr int R = kKAhead + 1;
-      if constexpr (ks + kKAhead < kSSteps) kf[(ks + kKAhead) % R] = kfrag(ks + kKAhead);
-      score_mfma(s, kf[ks % R], qf[ks], ks == 0);
-      if constexpr (WC && ks % 4 == 1 && ks / 4 < kCopiesW) {
-        if (cs.on) copy_one(cs, cc_slot, std::integral_constant<int, ks / 4>{});
-      }
+    static_for<0, kSSteps / 2>([&](auto pc_) {
+      constexpr int k0 = 2 * decltype(pc_)::value;
+      if constexpr (k0 + kKAhead < kSSteps) kf[(k0 + kKAhead) % R] = kfrag(k0 + kKAhead);
+      if constexpr (k0 + 1 + kKAhead < kSSteps) kf[(k0 + 1 + kKAhead) % R] = kfrag(k0 + 1 + kKAhead);
+      score_mfma2(s, kf[k0 % R], kf[(k0 + 1) % R], qf[k0], qf[k0 + 1], k0 == 0);
+      if constexpr (WC && k0 % 4 == 0) copy_one(rsrc, cc_slot, std::integral_constant<int, k0 / 4>{});
       __builtin_amdgcn_sched_barrier(0);
     });
-    if constexpr (WC) issued = cs.on;
   };
 
   // ---- softmax of the scored chunk D (scores in s), in 32 pieces; piece q
@@ -577,24 +574,28 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-      for (int b = 0; b < 2; ++b) vb[cb][b] = launder(lds + slot_off + voff(opaque(lane), cb, b));
+      for (int b = 0; b < 2; ++b) vb[cb][b] = launder(lds + slot_off + (v_lane ^ (64u * cb + 32u * b)));
     auto vfrag = [&](int f) -> bf16x8 {
       const int kk = f >> 4, ct = f & 15;
       const uint32_t off = 4096u * (ct >> 1) + 2048u * kk;
       const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb[ct & 1][0] + off));
-      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb[ct & 1][1] + off));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb[ct & 1][1] + off + 1024u));
       return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     };
-    bf16x8 vf[kVAhead + 1];
+    constexpr int R = kVAhead + 2;
+    bf16x8 vf[R];
 #pragma unroll
     for (int f = 0; f < kVAhead; ++f) vf[f] = vfrag(f);
     __builtin_amdgcn_sched_barrier(0);
-    static_for<0, 2 * kColTiles>([&](auto fc) {
-      constexpr int f = decltype(fc)::value;
-      constexpr int R = kVAhead + 1;
+    static_for<0, kColTiles>([&](auto gc) {
+      constexpr int f = 2 * decltype(gc)::value;  // fragments f, f + 1: tiles f & 15, (f & 15) + 1 of k-step f >> 4
       if constexpr (f + kVAhead < 2 * kColTiles) vf[(f + kVAhead) % R] = vfrag(f + kVAhead);
-      value_mfma<(f & 15)>(vf[f % R], pc[f >> 4]);
-      if constexpr (WS) smax_piece(fc, D);
+      if constexpr (f + 1 + kVAhead < 2 * kColTiles) vf[(f + 1 + kVAhead) % R] = vfrag(f + 1 + kVAhead);
+      value_mfma2<(f & 15)>(vf[f % R], vf[(f + 1) % R], pc[f >> 4]);
+      if constexpr (WS) {
+        smax_piece(std::integral_constant<int, f>{}, D);
+        smax_piece(std::integral_constant<int, f + 1>{}, D);
+      }
       __builtin_amdgcn_sched_barrier(0);
     });
   };
@@ -660,7 +661,6 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
     const uint32_t slot0 = (uint32_t)(t & 3) * kTileBytes;
     const uint32_t slot1 = (uint32_t)((t + 1) & 3) * kTileBytes;
     const uint32_t slot3 = lds_addr + (uint32_t)((t + 3) & 3) * kTileBytes;
-    bool issued = false;
 
     // the values enter a new segment / close one
     if (D0.valid() && D0.first) {
@@ -695,14 +695,18 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
       if (v_has) value_loop(slot0, std::false_type{}, D1);
       if (D0.valid() && D0.last) segment_end(D0);
       queries_ready();
-      if (s_has) score_loop(slot1, std::false_type{}, D3, slot3, issued);
+      if (s_has)
+        score_loop(slot1, std::false_type{}, D3, slot3);
+      else
+        s = f32x16{};
       static_for<0, 2 * kColTiles>([&](auto qc) { smax_piece(qc, D1); });
-      issued = copy_chunk(D3, slot3);
+      copy_chunk(D3, slot3);
     } else {
       if (s_has) {
-        score_loop(slot1, std::true_type{}, D3, slot3, issued);
+        score_loop(slot1, std::true_type{}, D3, slot3);
       } else {
-        issued = copy_chunk(D3, slot3);
+        copy_chunk(D3, slot3);
+        s = f32x16{};
       }
       if (v_has)
         value_loop(slot0, std::true_type{}, D1);
@@ -712,12 +716,10 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
     }
 
     // ---- end of step: this wave's share of chunk t + 2 has landed (that of
-    // chunk t + 3, the last vector memory loads issued, may still be in flight)
+    // chunk t + 3, the last nine vector memory loads issued, may still be in
+    // flight; loads complete in order)
     static_assert(kCopiesW == 9, "vmcnt below");
-    if (issued)
-      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
     block_sync();
     D0 = D1;
     D1 = D2;
