@@ -63,6 +63,64 @@ def check_fixed_agprs(src: str) -> None:
         if bad:
             raise RuntimeError(f"{src}: the compiler uses AGPRs reserved for the accumulators "
                                f"(register pressure too high?): {bad[:4]}")
+        check_mfma_operand_hazards(out, src)
+
+
+_REG = re.compile(r"([va])\[(\d+):(\d+)\]|([va])(\d+)\b")
+
+
+def _regs(tok: str):
+    out = set()
+    for m in _REG.finditer(tok):
+        if m.group(1):
+            out |= {(m.group(1), i) for i in range(int(m.group(2)), int(m.group(3)) + 1)}
+        else:
+            out.add((m.group(4), int(m.group(5))))
+    return out
+
+
+def check_mfma_operand_hazards(asm_path: str, src: str) -> None:
+    """Fail if a VALU write reaches an MFMA operand with fewer than 2 wait states.
+
+    The kernel's MFMAs are inline assembly, so the compiler's hazard recognizer
+    does not see them; this checks the straight-line code before each one (a
+    label within reach is treated as a hazard too).
+    """
+    insts = []
+    with open(asm_path) as f:
+        for line in f:
+            code = line.split(";", 1)[0].rstrip()
+            if not code.strip():
+                continue
+            if not code.startswith("\t"):
+                if code.endswith(":"):
+                    insts.append("LABEL")
+                continue
+            t = code.strip()
+            if not t.startswith("."):
+                insts.append(t)
+    bad = []
+    for k, t in enumerate(insts):
+        if not t.startswith("v_mfma"):
+            continue
+        src_regs = _regs(",".join(t.split(None, 1)[1].split(",")[1:4]))
+        ws = 0
+        for j in range(k - 1, max(k - 4, -1), -1):
+            pt = insts[j]
+            if pt == "LABEL":
+                bad.append(f"label right before {t}")
+                break
+            if pt.startswith("s_nop"):
+                ws += int(pt.split()[-1]) + 1
+            else:
+                if pt.startswith("v_") and not pt.startswith("v_mfma") and len(pt.split()) > 1:
+                    if _regs(pt.split(None, 1)[1].split(",")[0]) & src_regs and ws < 2:
+                        bad.append(f"{pt} -> {t}")
+                ws += 1
+            if ws >= 2:
+                break
+    if bad:
+        raise RuntimeError(f"{src}: VALU result feeds an MFMA too early: {bad[:4]}")
 
 
 def build(verbose: bool = False) -> str:

@@ -600,8 +600,11 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
     });
   };
 
-  // ---- the end of chunk D0's segment: this wave's rows of out (or of the
-  // split's fp32 partial) and lse; then clear the accumulators
+  // ---- the end of chunk D0's segment: this wave's rows of out and lse, or,
+  // for a split sequence, its bf16 partial (O / l) and lse; then clear the
+  // accumulators.  The partial of a split keeps the accumulator layout: per
+  // 32-row tile, tile ct and element pair gp, 64 lanes x 16 bytes (elements
+  // 8 gp .. 8 gp + 7 of the lane's 16), so every store is 1 KB contiguous.
   auto segment_end = [&](const Chunk& D0) {
     float inv = seg_inv, lse = seg_lse;
     if (seg_bad) {
@@ -611,25 +614,28 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
     mfma_result_wait();
     const RowInfo ri = row_info();
     const int row = ri.row;
-    if (ri.ok) {
-      const int col0 = 4 * hlf;
-      if (seg_nsplit == 1) {
+    if (seg_nsplit == 1) {
+      if (ri.ok) {
         uint16_t* op =
-            a.out + (int64_t)D0.seq * a.o_sb + (int64_t)ri.qi * a.o_ss + (int64_t)ri.hh * a.o_sh + col0;
+            a.out + (int64_t)D0.seq * a.o_sb + (int64_t)ri.qi * a.o_ss + (int64_t)ri.hh * a.o_sh + 4 * hlf;
         static_for<0, 4 * kColTiles>([&](auto ic) {
           constexpr int I = decltype(ic)::value;  // tile I >> 2, elements 4 (I & 3) ..
           const f32x4 v = acc_read4<I>() * inv;
           *(bf16x4*)(op + 32 * (I >> 2) + 8 * (I & 3)) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
         });
         if (hlf == 0) a.lse[(int64_t)D0.seq * a.l_sb + (int64_t)ri.qi * a.l_ss + (int64_t)ri.hh * a.l_sh] = lse;
-      } else {
-        float* pp = a.part_o + ((int64_t)seg_slot * a.rows + row) * kDv + col0;
-        static_for<0, 4 * kColTiles>([&](auto ic) {
-          constexpr int I = decltype(ic)::value;
-          *(f32x4*)(pp + 32 * (I >> 2) + 8 * (I & 3)) = acc_read4<I>() * inv;
-        });
-        if (hlf == 0) a.part_lse[(int64_t)seg_slot * a.rows + row] = lse;
       }
+    } else if (pi.blk_row0 + 32 * w < a.rows) {
+      // (rows past the last one store zeros into the tile's padding)
+      uint8_t* pb = (uint8_t*)a.part_o + (int64_t)seg_slot * partial_slot_bytes(a.rows) +
+                    (int64_t)((pi.blk_row0 >> 5) + w) * kPartialTileBytes + 16 * opaque(lane);
+      static_for<0, 2 * kColTiles>([&](auto ic) {
+        constexpr int I = decltype(ic)::value;  // tile I >> 1, elements 8 (I & 1) ..
+        const f32x4 v0 = acc_read4<2 * I>() * inv, v1 = acc_read4<2 * I + 1>() * inv;
+        *(bf16x8*)(pb + 1024 * I) = bf16x8{(__bf16)v0[0], (__bf16)v0[1], (__bf16)v0[2], (__bf16)v0[3],
+                                           (__bf16)v1[0], (__bf16)v1[1], (__bf16)v1[2], (__bf16)v1[3]};
+      });
+      if (ri.ok && hlf == 0) a.part_lse[(int64_t)seg_slot * a.rows + row] = lse;
     }
     acc_zero();
     asm volatile("s_nop 4" ::: "memory");

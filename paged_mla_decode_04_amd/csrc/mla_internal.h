@@ -21,12 +21,22 @@ struct DecodeArgs {
   const int32_t* num_splits;
   int32_t num_parts, row_blocks;
   float* part_lse;             // [slots][rows]
-  float* part_o;               // [slots][rows][512]
+  float* part_o;               // narrow kernel: fp32 [slots][rows][512]; wide kernel: bf16 tiles (below)
   uint16_t* out;               // bf16 bits
   int64_t o_sb, o_ss, o_sh;
   float* lse;
   int64_t l_sb, l_ss, l_sh;
 };
+
+// Wide kernel partials: per slot, ceil(rows / 32) tiles of 32 rows x 512
+// columns in bf16 (32 KB), stored in the accumulator layout: [tile][column
+// tile ct (16)][element pair gp (2)][lane (64)][8 bf16].  A lane (j = lane & 31,
+// h = lane >> 5) holds row j, columns 32 ct + 8 g + 4 h + e for g = 2 gp,
+// 2 gp + 1 and e = 0..3.
+constexpr int kPartialTileBytes = 32 * 512 * 2;
+__host__ __device__ inline int64_t partial_slot_bytes(int rows) {
+  return (int64_t)((rows + 31) / 32) * kPartialTileBytes;
+}
 
 hipError_t launch_plan(const int32_t* seqlens, int batch, int rows, int num_parts, int32_t* tile_md,
                        int32_t* num_splits, hipStream_t stream);

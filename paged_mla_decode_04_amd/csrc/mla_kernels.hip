@@ -588,6 +588,93 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   if (lane == 0) a.lse[(int64_t)b * a.l_sb + (int64_t)qi * a.l_ss + (int64_t)h * a.l_sh] = L;
 }
 
+// The same merge for the wide kernel's bf16 tile partials: one workgroup per
+// (sequence, 32-row tile); wave v merges column tiles 4 v .. 4 v + 3 of the
+// 32 rows in the accumulator layout the partials keep, then the tile goes
+// through LDS so that every output row is written as one 1 KB store.
+__global__ __launch_bounds__(256) void combine_tiles_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[32][kDv + 8];
+  const int b = blockIdx.x, rt = blockIdx.y;
+  const int base = a.num_splits[b];
+  const int ns = a.num_splits[b + 1] - base;
+  if (ns <= 1) return;
+  const int v = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int j = lane & 31, h = lane >> 5;
+  const int row = 32 * rt + j;
+  const bool ok = row < a.rows;
+  // this lane's row: L = log sum exp(lse_i) (NaN if any partial is NaN)
+  float mx = -INFINITY;
+  bool nan = false;
+  for (int i = 0; i < ns; ++i) {
+    const float x = ok ? a.part_lse[(int64_t)(base + i) * a.rows + row] : -INFINITY;
+    nan |= (x != x);
+    mx = fmaxf(mx, x);
+  }
+  float L = -INFINITY;
+  if (mx != -INFINITY) {
+    float sum = 0.f;
+    for (int i = 0; i < ns; ++i) {
+      const float x = ok ? a.part_lse[(int64_t)(base + i) * a.rows + row] : -INFINITY;
+      sum += __builtin_amdgcn_exp2f((x - mx) * kLog2e);
+    }
+    L = mx + __builtin_amdgcn_logf(sum) * kLn2;
+  }
+  float acc[8][8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[p][e] = 0.f;
+  if (L != -INFINITY) {
+    for (int i = 0; i < ns; ++i) {
+      const float x = ok ? a.part_lse[(int64_t)(base + i) * a.rows + row] : -INFINITY;
+      const float wgt = __builtin_amdgcn_exp2f((x - L) * kLog2e);
+      const uint8_t* src = (const uint8_t*)a.part_o + (int64_t)(base + i) * partial_slot_bytes(a.rows) +
+                           (int64_t)rt * kPartialTileBytes + 8 * 1024 * v + 16 * lane;
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const bf16x8 pv = *(const bf16x8*)(src + 1024 * p);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[p][e] += wgt * (float)pv[e];
+      }
+    }
+  }
+  if (nan) {
+    L = __builtin_nanf("");
+#pragma unroll
+    for (int p = 0; p < 8; ++p)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[p][e] = __builtin_nanf("");
+  }
+  // pair p of wave v: column tile ct = 4 v + (p >> 1), elements of g = 2 (p & 1) + (e >> 2)
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int ct = 4 * v + (p >> 1);
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg) {
+      const int col = 32 * ct + 8 * (2 * (p & 1) + gg) + 4 * h;
+      bf16x4 o4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o4[e] = (__bf16)acc[p][4 * gg + e];
+      *(bf16x4*)&tile[j][col] = o4;
+    }
+  }
+  if (v == 0 && h == 0 && ok) {
+    const int qi = row / a.h_q, hh = row - qi * a.h_q;
+    a.lse[(int64_t)b * a.l_sb + (int64_t)qi * a.l_ss + (int64_t)hh * a.l_sh] = L;
+  }
+  __syncthreads();
+  // wave v writes rows 8 v .. 8 v + 7, 64 lanes x 16 bytes each
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int jr = 8 * v + r, orow = 32 * rt + jr;
+    if (orow < a.rows) {
+      const int qi = orow / a.h_q, hh = orow - qi * a.h_q;
+      uint16_t* op = a.out + (int64_t)b * a.o_sb + (int64_t)qi * a.o_ss + (int64_t)hh * a.o_sh + 8 * lane;
+      *(bf16x8*)op = *(const bf16x8*)&tile[jr][8 * lane];
+    }
+  }
+}
+
 // Block-wide inclusive scan step over one 1024-entry chunk (16 waves).
 template <typename T>
 __device__ __forceinline__ T block_inclusive_scan(T v, T* wave_tot, T* carry) {
@@ -665,6 +752,11 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream) {
+  if (rows_per_block(a.rows) == kRowsPerWorkgroup) {
+    const dim3 grid((unsigned)a.batch, (unsigned)((a.rows + 31) / 32));
+    hipLaunchKernelGGL(combine_tiles_kernel, grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)a.batch, (unsigned)((a.rows + 3) / 4));
   hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
