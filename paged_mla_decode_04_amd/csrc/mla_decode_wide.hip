@@ -496,15 +496,18 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
   // ---- softmax of the scored chunk D (scores in s), in 32 pieces; piece q
   // runs after value MFMA q when interleaved
   float mu = 0.f;
-  auto smax_piece = [&](auto qc, const Chunk& D) {
+  // (FAST: a full chunk inside its segment that no row's limit reaches:
+  // no masking and no segment results)
+  auto smax_piece = [&](auto qc, const Chunk& D, auto fast_tag) {
     constexpr int q = decltype(qc)::value;
+    constexpr bool FAST = decltype(fast_tag)::value;
     if constexpr (q == 0) {
       mfma_result_wait();
       mu = m_ref == -INFINITY ? 0.f : m_ref;
     } else if constexpr (q >= 1 && q <= 4) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) s[4 * (q - 1) + e] = __builtin_fmaf(s[4 * (q - 1) + e], sc, -mu);
-    } else if constexpr (q == 5) {
+    } else if constexpr (q == 5 && !FAST) {
       // keys past the row's limit (only chunks that reach the smallest limit)
       const int tok0 = kChunk * D.chunk;
       if (D.tok <= 0 || tok0 + kChunk > lim_min) {
@@ -556,7 +559,7 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = (__bf16)s[8 * kk + e];
       pc[kk] = v;
-    } else if constexpr (q == 30) {
+    } else if constexpr (q == 30 && !FAST) {
       if (D.last) {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(lsum), __float_as_int(lsum), false, false);
         const float l = __int_as_float(sw[0]) + __int_as_float(sw[1]);
@@ -568,8 +571,11 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
 
   // ---- the value product of chunk t (slot at slot_off), optionally with the
   // softmax of chunk D between its MFMAs
+  // with_smax: 0 = values only, 1 = with the softmax of D, 2 = with the fast
+  // softmax of D
   auto value_loop = [&](uint32_t slot_off, auto with_smax, const Chunk& D) {
-    constexpr bool WS = decltype(with_smax)::value;
+    constexpr int WS = decltype(with_smax)::value;
+    constexpr std::integral_constant<bool, WS == 2> fast_tag{};
     lds_u8* vb[2][2];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
@@ -592,9 +598,9 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
       if constexpr (f + kVAhead < 2 * kColTiles) vf[(f + kVAhead) % R] = vfrag(f + kVAhead);
       if constexpr (f + 1 + kVAhead < 2 * kColTiles) vf[(f + 1 + kVAhead) % R] = vfrag(f + 1 + kVAhead);
       value_mfma2<(f & 15)>(vf[f % R], vf[(f + 1) % R], pc[f >> 4]);
-      if constexpr (WS) {
-        smax_piece(std::integral_constant<int, f>{}, D);
-        smax_piece(std::integral_constant<int, f + 1>{}, D);
+      if constexpr (WS != 0) {
+        smax_piece(std::integral_constant<int, f>{}, D, fast_tag);
+        smax_piece(std::integral_constant<int, f + 1>{}, D, fast_tag);
       }
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -668,57 +674,66 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
     const uint32_t slot1 = (uint32_t)((t + 1) & 3) * kTileBytes;
     const uint32_t slot3 = lds_addr + (uint32_t)((t + 3) & 3) * kTileBytes;
 
-    // the values enter a new segment / close one
-    if (D0.valid() && D0.first) {
-      const int split = D0.seq == pi.seq_begin ? pi.split_first : 0;
-      const int s0 = ((cint32*)a.num_splits)[D0.seq];
-      seg_slot = s0 + split;
-      seg_nsplit = ((cint32*)a.num_splits)[D0.seq + 1] - s0;
-      seg_bad = false;
-    }
-    if (D0.valid()) {
-      seg_bad |= D0.bad;
-      if (D0.last) {
-        seg_inv = cap_inv;
-        seg_lse = cap_lse;
-      }
-    }
-    // the reference max of some rows moved at chunk t: rescale their sums
-    if (pending) {
-      if (v_has) {
-        mfma_result_wait();
-        acc_scale(pend_f);
-        asm volatile("s_nop 4" ::: "memory");
-      }
-      pending = false;
-      pend_f = 1.f;
-    }
-
-    if (D1.valid() && D1.first && t >= 0) {
-      // ---- a new segment is scored: queries first, values of chunk t, the
-      // end of its segment, then the scores and the softmax
-      load_queries(D1);
-      if (v_has) value_loop(slot0, std::false_type{}, D1);
-      if (D0.valid() && D0.last) segment_end(D0);
-      queries_ready();
-      if (s_has)
-        score_loop(slot1, std::false_type{}, D3, slot3);
-      else
-        s = f32x16{};
-      static_for<0, 2 * kColTiles>([&](auto qc) { smax_piece(qc, D1); });
-      copy_chunk(D3, slot3);
+    // the common step: full chunks inside one segment, no limit reached, no
+    // pending rescale -- no segment bookkeeping, no masking, no results
+    const bool fast = t >= 0 && v_has && D1.valid() && D1.tok == kChunk && !D0.first && !D0.last && !D0.bad &&
+                      !D1.first && !D1.last && !pending && kChunk * (D1.chunk + 1) <= lim_min;
+    if (fast) {
+      score_loop(slot1, std::true_type{}, D3, slot3);
+      value_loop(slot0, std::integral_constant<int, 2>{}, D1);
     } else {
-      if (s_has) {
-        score_loop(slot1, std::true_type{}, D3, slot3);
-      } else {
-        copy_chunk(D3, slot3);
-        s = f32x16{};
+      // the values enter a new segment / close one
+      if (D0.valid() && D0.first) {
+        const int split = D0.seq == pi.seq_begin ? pi.split_first : 0;
+        const int s0 = ((cint32*)a.num_splits)[D0.seq];
+        seg_slot = s0 + split;
+        seg_nsplit = ((cint32*)a.num_splits)[D0.seq + 1] - s0;
+        seg_bad = false;
       }
-      if (v_has)
-        value_loop(slot0, std::true_type{}, D1);
-      else if (D1.valid())
-        static_for<0, 2 * kColTiles>([&](auto qc) { smax_piece(qc, D1); });
-      if (D0.valid() && D0.last) segment_end(D0);
+      if (D0.valid()) {
+        seg_bad |= D0.bad;
+        if (D0.last) {
+          seg_inv = cap_inv;
+          seg_lse = cap_lse;
+        }
+      }
+      // the reference max of some rows moved at chunk t: rescale their sums
+      if (pending) {
+        if (v_has) {
+          mfma_result_wait();
+          acc_scale(pend_f);
+          asm volatile("s_nop 4" ::: "memory");
+        }
+        pending = false;
+        pend_f = 1.f;
+      }
+
+      if (D1.valid() && D1.first && t >= 0) {
+        // ---- a new segment is scored: queries first, values of chunk t, the
+        // end of its segment, then the scores and the softmax
+        load_queries(D1);
+        if (v_has) value_loop(slot0, std::integral_constant<int, 0>{}, D1);
+        if (D0.valid() && D0.last) segment_end(D0);
+        queries_ready();
+        if (s_has)
+          score_loop(slot1, std::false_type{}, D3, slot3);
+        else
+          s = f32x16{};
+        static_for<0, 2 * kColTiles>([&](auto qc) { smax_piece(qc, D1, std::false_type{}); });
+        copy_chunk(D3, slot3);
+      } else {
+        if (s_has) {
+          score_loop(slot1, std::true_type{}, D3, slot3);
+        } else {
+          copy_chunk(D3, slot3);
+          s = f32x16{};
+        }
+        if (v_has)
+          value_loop(slot0, std::integral_constant<int, 1>{}, D1);
+        else if (D1.valid())
+          static_for<0, 2 * kColTiles>([&](auto qc) { smax_piece(qc, D1, std::false_type{}); });
+        if (D0.valid() && D0.last) segment_end(D0);
+      }
     }
 
     // ---- end of step: this wave's share of chunk t + 2 has landed (that of
