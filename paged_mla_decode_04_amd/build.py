@@ -83,10 +83,11 @@ def check_mfma_operand_hazards(asm_path: str, src: str) -> None:
     """Fail if a VALU write reaches an MFMA operand with fewer than 2 wait states.
 
     The kernel's MFMAs are inline assembly, so the compiler's hazard recognizer
-    does not see them; this checks the straight-line code before each one (a
-    label within reach is treated as a hazard too).
+    does not see them; this walks back from each one over every control-flow
+    path (fall-through and every branch into a label on the way), counting
+    wait states; a branch instruction itself is not counted as one.
     """
-    insts = []
+    insts = []    # instruction text, or ("LABEL", name)
     with open(asm_path) as f:
         for line in f:
             code = line.split(";", 1)[0].rstrip()
@@ -94,31 +95,49 @@ def check_mfma_operand_hazards(asm_path: str, src: str) -> None:
                 continue
             if not code.startswith("\t"):
                 if code.endswith(":"):
-                    insts.append("LABEL")
+                    insts.append(("LABEL", code[:-1]))
                 continue
             t = code.strip()
             if not t.startswith("."):
                 insts.append(t)
-    bad = []
+    branches = {}  # label name -> indexes of the branches that target it
     for k, t in enumerate(insts):
-        if not t.startswith("v_mfma"):
-            continue
-        src_regs = _regs(",".join(t.split(None, 1)[1].split(",")[1:4]))
-        ws = 0
-        for j in range(k - 1, max(k - 4, -1), -1):
+        if isinstance(t, str) and (t.startswith("s_cbranch") or t.startswith("s_branch")):
+            branches.setdefault(t.split()[-1], []).append(k)
+
+    def ends_flow(t) -> bool:
+        return isinstance(t, str) and (t.startswith("s_branch") or t.startswith("s_endpgm")
+                                       or t.startswith("s_setpc"))
+
+    bad = []
+
+    def walk(j: int, ws: int, src_regs: set, mfma: str, seen: set) -> None:
+        while j >= 0 and ws < 2:
             pt = insts[j]
-            if pt == "LABEL":
-                bad.append(f"label right before {t}")
-                break
+            if isinstance(pt, tuple):
+                for b in branches.get(pt[1], []):
+                    if (b, ws) not in seen:
+                        seen.add((b, ws))
+                        walk(b - 1, ws, src_regs, mfma, seen)
+                if j == 0 or ends_flow(insts[j - 1]):
+                    return
+                j -= 1
+                continue
+            if pt.startswith("s_cbranch") or pt.startswith("s_branch"):
+                j -= 1
+                continue
             if pt.startswith("s_nop"):
-                ws += int(pt.split()[-1]) + 1
+                ws += int(pt.split()[-1], 0) + 1
             else:
                 if pt.startswith("v_") and not pt.startswith("v_mfma") and len(pt.split()) > 1:
-                    if _regs(pt.split(None, 1)[1].split(",")[0]) & src_regs and ws < 2:
-                        bad.append(f"{pt} -> {t}")
+                    if _regs(pt.split(None, 1)[1].split(",")[0]) & src_regs:
+                        bad.append(f"{pt} -> {mfma}")
                 ws += 1
-            if ws >= 2:
-                break
+            j -= 1
+
+    for k, t in enumerate(insts):
+        if isinstance(t, str) and t.startswith("v_mfma"):
+            walk(k - 1, 0, _regs(",".join(t.split(None, 1)[1].split(",")[1:4])), t, set())
     if bad:
         raise RuntimeError(f"{src}: VALU result feeds an MFMA too early: {bad[:4]}")
 
