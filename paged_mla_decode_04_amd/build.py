@@ -40,7 +40,7 @@ _ASM_AGPR = re.compile(r"accvgpr|\ba\[\d|[ ,]a\d+\b")
 
 
 def check_fixed_agprs(src: str) -> None:
-    """Fail if the compiler itself references AGPRs in the kernel's assembly."""
+    """Fail if the compiler itself references AGPRs, or spills VGPRs, in the kernel's assembly."""
     with tempfile.TemporaryDirectory() as td:
         out = os.path.join(td, "k.s")
         cmd = [hipcc(), *HIPCC_FLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out]
@@ -63,6 +63,10 @@ def check_fixed_agprs(src: str) -> None:
         if bad:
             raise RuntimeError(f"{src}: the compiler uses AGPRs reserved for the accumulators "
                                f"(register pressure too high?): {bad[:4]}")
+        with open(out) as f:
+            spills = [int(m.group(1)) for m in re.finditer(r"\.vgpr_spill_count:\s+(\d+)", f.read())]
+        if any(spills):
+            raise RuntimeError(f"{src}: the compiler spills VGPRs to scratch memory ({spills})")
         check_mfma_operand_hazards(out, src)
 
 

@@ -503,7 +503,9 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
     constexpr bool FAST = decltype(fast_tag)::value;
     if constexpr (q == 0) {
       mfma_result_wait();
-      mu = m_ref == -INFINITY ? 0.f : m_ref;
+      // (a common step's reference is finite: its segment's first chunk had
+      // visible keys in every row)
+      mu = FAST ? m_ref : (m_ref == -INFINITY ? 0.f : m_ref);
     } else if constexpr (q >= 1 && q <= 4) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) s[4 * (q - 1) + e] = __builtin_fmaf(s[4 * (q - 1) + e], sc, -mu);
@@ -522,7 +524,7 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
       float mx = s[0];
 #pragma unroll
       for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
-      const bool over = m_ref == -INFINITY ? mx > -INFINITY : mx > kRescaleSlack;
+      const bool over = FAST ? mx > kRescaleSlack : (m_ref == -INFINITY ? mx > -INFINITY : mx > kRescaleSlack);
       if (__builtin_amdgcn_ballot_w64(over) != 0) {
         // a chunk max passed the reference by more than 2^16 (or the segment
         // just started): move the row's reference to its max
