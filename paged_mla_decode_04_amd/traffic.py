@@ -27,7 +27,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 1 << 30                     # bench.py --copy-probe copies 1 GiB
-DECODE_KERNELS = ("decode_kernel", "combine_kernel")
+DECODE_KERNELS = ("decode", "combine")  # name parts of the kernels a decode call launches
 
 
 def source_hash() -> str:
@@ -67,9 +67,14 @@ def summarize(copy_fetch: str, copy_write: str, fetch: str, write: str, workload
     f = _per_dispatch_kib(fetch, "FETCH_SIZE")
     w = _per_dispatch_kib(write, "WRITE_SIZE")
     kernels = {}
-    for k in DECODE_KERNELS:
-        kernels[k] = {"fetch_bytes": _pick(f, k) * 1024.0 * fetch_scale,
-                      "write_bytes": _pick(w, k) * 1024.0 * write_scale}
+    for name in sorted(f):
+        if any(k in name for k in DECODE_KERNELS) and name in w:
+            short = name.rsplit("(", 1)[0].replace("void ", "").replace("(anonymous namespace)::", "")
+            short = short.replace("mla::", "")
+            kernels[short] = {"fetch_bytes": f[name] * 1024.0 * fetch_scale,
+                              "write_bytes": w[name] * 1024.0 * write_scale}
+    if not kernels:
+        raise ValueError(f"no decode or combine kernel among {sorted(f)}")
     total = sum(v["fetch_bytes"] + v["write_bytes"] for v in kernels.values())
     return {
         "workload": workload,

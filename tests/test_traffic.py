@@ -24,15 +24,19 @@ def test_summary_scales_by_the_copy_calibration(tmp_path):
     write_csv(tmp_path / "cw.csv", "WRITE_SIZE", {"__amd_rocclr_copyBuffer": [gib_kib]})
     write_csv(tmp_path / "f.csv", "FETCH_SIZE", {"void mla::decode_kernel<4>(mla::DecodeArgs)": [100.0, 300.0],
                                                  "mla::combine_kernel(mla::DecodeArgs)": [10.0],
+                                                 "mla::(anonymous namespace)::decode_wide_kernel(mla::DecodeArgs)": [8.0],
                                                  "mla::plan_kernel(int const*)": [1.0]})
     write_csv(tmp_path / "w.csv", "WRITE_SIZE", {"void mla::decode_kernel<4>(mla::DecodeArgs)": [50.0],
+                                                 "mla::(anonymous namespace)::decode_wide_kernel(mla::DecodeArgs)": [4.0],
                                                  "mla::combine_kernel(mla::DecodeArgs)": [5.0, 7.0]})
     d = traffic.summarize(str(tmp_path / "cf.csv"), str(tmp_path / "cw.csv"), str(tmp_path / "f.csv"),
                           str(tmp_path / "w.csv"), "wide")
     assert d["fetch_scale"] == 2.0 and d["write_scale"] == 1.0
-    assert d["kernels"]["decode_kernel"]["fetch_bytes"] == 200.0 * 1024 * 2
+    # the plan is not part of the call
+    assert sorted(d["kernels"]) == ["combine_kernel", "decode_kernel<4>", "decode_wide_kernel"]
+    assert d["kernels"]["decode_kernel<4>"]["fetch_bytes"] == 200.0 * 1024 * 2
     assert d["kernels"]["combine_kernel"]["write_bytes"] == 6.0 * 1024
-    assert d["bytes_per_call"] == (200 * 2 + 50 + 10 * 2 + 6) * 1024
+    assert d["bytes_per_call"] == (200 * 2 + 50 + 10 * 2 + 6 + 8 * 2 + 4) * 1024
     assert d["source_sha256"] == traffic.source_hash()
     json.dumps(d)
 
