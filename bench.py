@@ -18,6 +18,7 @@ Prints one JSON line.  Runs on one GPU only.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -52,7 +53,49 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (calibrates HBM byte counters)")
+    # layout and shape overrides of the chosen workload (ablations and sweeps)
+    ap.add_argument("--pitch", type=int, choices=(576, 640), default=None,
+                    help="cache entry pitch in elements (the pad is never read)")
+    ap.add_argument("--table", choices=("arange", "randperm"), default=None,
+                    help="identity or seeded-permutation block table")
+    ap.add_argument("--seqlen-mean", type=int, default=None,
+                    help="seqlens ~ N(mean, mean/4) clipped to [1, 2 mean] instead of the recipe")
+    ap.add_argument("--s-q", type=int, default=None, help="query tokens per sequence")
+    ap.add_argument("--h-q", type=int, default=None, help="query heads")
+    ap.add_argument("--causal", choices=("yes", "no"), default=None)
+    ap.add_argument("--flush", action="store_true",
+                    help="write 512 MB before every timed step so that no input stays in L2 or the "
+                         "256 MB Infinity Cache; the step time is then taken from HIP events")
     return ap.parse_args()
+
+
+def chosen_workload(args):
+    """The named workload with any layout or shape overrides applied (renamed if changed)."""
+    w = WORKLOADS[args.workload]
+    changes, tags = {}, []
+    if args.pitch is not None and args.pitch != w.pitch:
+        changes["pitch"] = args.pitch
+        tags.append(f"pitch {args.pitch}")
+    if args.table is not None and args.table != w.table:
+        changes["table"] = args.table
+        tags.append(f"{'identity' if args.table == 'arange' else 'permuted'} table")
+    if args.seqlen_mean is not None:
+        m = int(args.seqlen_mean)
+        changes["seqlens"] = f"normal_{m}_{max(1, m // 4)}"
+        tags.append(f"seqlens ~ N({m},{max(1, m // 4)}) clipped to [1,{2 * m}]")
+    if args.s_q is not None and args.s_q != w.s_q:
+        changes["s_q"] = args.s_q
+        tags.append(f"s_q={args.s_q}")
+    if args.h_q is not None and args.h_q != w.h_q:
+        changes["h_q"] = args.h_q
+        tags.append(f"h_q={args.h_q}")
+    if args.causal is not None and (args.causal == "yes") != w.causal:
+        changes["causal"] = args.causal == "yes"
+        tags.append("causal" if args.causal == "yes" else "non-causal")
+    if not changes:
+        return w
+    return dataclasses.replace(w, name=w.name + "+" + "+".join(t.split()[0] for t in tags),
+                               description=w.description + "; with " + ", ".join(tags), **changes)
 
 
 def copy_probe():
@@ -117,7 +160,7 @@ def main():
         return
     _lib.load()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
-    inp_host = draw(args.workload)
+    inp_host = draw(chosen_workload(args))
     inp = inp_host.to(dev)
     w = inp.workload
     rows = w.s_q * w.h_q
@@ -142,9 +185,12 @@ def main():
     # timed region: exactly `steps` steps; events bracket the decode call of each
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    flush = torch.empty((512 << 20,), dtype=torch.uint8, device=dev) if args.flush else None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for e0, e1, e2 in ev:
+    for i, (e0, e1, e2) in enumerate(ev):
+        if flush is not None:
+            flush.fill_(i & 255)
         e0.record()
         meta = get_mla_metadata(inp.cache_seqlens, rows, w.h_kv, num_parts=parts)
         e1.record()
@@ -155,6 +201,8 @@ def main():
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
     ms_per_step = wall_ms / args.steps
+    if flush is not None:  # the flush is not part of a step
+        ms_per_step = float(np.mean([a.elapsed_time(c) for a, _, c in ev]))
     plan_ms = float(np.mean([a.elapsed_time(b_) for a, b_, _ in ev]))
     decode_ms = np.array([b_.elapsed_time(c) for _, b_, c in ev])
 
@@ -181,7 +229,8 @@ def main():
         "config": {
             "workload": f"{w.name}: {w.description}",
             "batch": b, "s_q": w.s_q, "h_q": w.h_q, "h_kv": w.h_kv, "d": 576, "dv": 512,
-            "block_size": 64, "entry_pitch": w.pitch, "causal": w.causal,
+            "block_size": 64, "entry_pitch": w.pitch, "block_table": w.table, "causal": w.causal,
+            "caches": "flushed before each step" if args.flush else "warm",
             "total_seqlens": cost["total_seqlens"], "num_parts": parts,
             "parallelism": "single GPU",
         },

@@ -536,6 +536,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     decode_role<NRT, false>(a, pi, lds, wave, lane);
 }
 
+constexpr int kMergeUnroll = 4;  // splits whose loads are in flight together
+
 // Merge the partials of every sequence that more than one part touched:
 // L = log(sum_i exp(lse_i)), out = sum_i exp(lse_i - L) * O_i (empty partials,
 // lse = -inf, weigh nothing; all empty gives out = 0, lse = -inf).
@@ -546,31 +548,54 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int base = a.num_splits[b];
   const int ns = a.num_splits[b + 1] - base;
   if (ns <= 1 || r >= a.rows) return;
-  float mx = -INFINITY;
+  const float* lse_p = a.part_lse + (int64_t)base * a.rows + r;
+  // L in one pass (online max and sum), four loads in flight
+  float mx = -INFINITY, sum = 0.f;
   bool nan = false;
-  for (int i = 0; i < ns; ++i) {
-    const float x = a.part_lse[(int64_t)(base + i) * a.rows + r];
-    nan |= (x != x);
-    mx = fmaxf(mx, x);
+  for (int i0 = 0; i0 < ns; i0 += kMergeUnroll) {
+    float x[kMergeUnroll];
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) x[u] = i0 + u < ns ? lse_p[(int64_t)(i0 + u) * a.rows] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      if (x[u] != x[u]) {
+        nan = true;
+      } else if (x[u] > mx) {
+        sum = sum * __builtin_amdgcn_exp2f((mx - x[u]) * kLog2e) + 1.f;
+        mx = x[u];
+      } else if (x[u] != -INFINITY) {
+        sum += __builtin_amdgcn_exp2f((x[u] - mx) * kLog2e);
+      }
+    }
   }
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float L = -INFINITY;
-  if (mx != -INFINITY) {
-    float sum = 0.f;
-    for (int i = 0; i < ns; ++i) {
-      const float x = a.part_lse[(int64_t)(base + i) * a.rows + r];
-      sum += __builtin_amdgcn_exp2f((x - mx) * kLog2e);
-    }
+  if (mx != -INFINITY && !nan) {
     L = mx + __builtin_amdgcn_logf(sum) * kLn2;
-    for (int i = 0; i < ns; ++i) {
-      const float x = a.part_lse[(int64_t)(base + i) * a.rows + r];
-      const float w = __builtin_amdgcn_exp2f((x - L) * kLog2e);
-      const f32x4* src = (const f32x4*)(a.part_o + ((int64_t)(base + i) * a.rows + r) * kDv + 8 * lane);
-      const f32x4 v0 = src[0], v1 = src[1];
+    const f32x4* src0 = (const f32x4*)(a.part_o + ((int64_t)base * a.rows + r) * kDv + 8 * lane);
+    for (int i0 = 0; i0 < ns; i0 += kMergeUnroll) {
+      float x[kMergeUnroll];
+      f32x4 v0[kMergeUnroll], v1[kMergeUnroll];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[j] += w * v0[j];
-        acc[4 + j] += w * v1[j];
+      for (int u = 0; u < kMergeUnroll; ++u) {
+        if (i0 + u < ns) {
+          x[u] = lse_p[(int64_t)(i0 + u) * a.rows];
+          const f32x4* src = src0 + (int64_t)(i0 + u) * a.rows * (kDv / 4);
+          v0[u] = src[0];
+          v1[u] = src[1];
+        } else {
+          x[u] = -INFINITY;
+          v0[u] = v1[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kMergeUnroll; ++u) {
+        const float w = __builtin_amdgcn_exp2f((x[u] - L) * kLog2e);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[j] += w * v0[u][j];
+          acc[4 + j] += w * v1[u][j];
+        }
       }
     }
   }
@@ -602,34 +627,40 @@ __global__ __launch_bounds__(256) void combine_tiles_kernel(DecodeArgs a) {
   const int j = lane & 31, h = lane >> 5;
   const int row = 32 * rt + j;
   const bool ok = row < a.rows;
-  // this lane's row: L = log sum exp(lse_i) (NaN if any partial is NaN)
-  float mx = -INFINITY;
+  // this lane's row: L = log sum exp(lse_i) (NaN if any partial is NaN), in
+  // one pass (online max and sum) with four loads in flight
+  const float* lse_p = a.part_lse + (int64_t)base * a.rows + row;
+  float mx = -INFINITY, sum = 0.f;
   bool nan = false;
-  for (int i = 0; i < ns; ++i) {
-    const float x = ok ? a.part_lse[(int64_t)(base + i) * a.rows + row] : -INFINITY;
-    nan |= (x != x);
-    mx = fmaxf(mx, x);
-  }
-  float L = -INFINITY;
-  if (mx != -INFINITY) {
-    float sum = 0.f;
-    for (int i = 0; i < ns; ++i) {
-      const float x = ok ? a.part_lse[(int64_t)(base + i) * a.rows + row] : -INFINITY;
-      sum += __builtin_amdgcn_exp2f((x - mx) * kLog2e);
+  for (int i0 = 0; i0 < ns; i0 += kMergeUnroll) {
+    float x[kMergeUnroll];
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) x[u] = (ok && i0 + u < ns) ? lse_p[(int64_t)(i0 + u) * a.rows] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      if (x[u] != x[u]) {
+        nan = true;
+      } else if (x[u] > mx) {
+        sum = sum * __builtin_amdgcn_exp2f((mx - x[u]) * kLog2e) + 1.f;
+        mx = x[u];
+      } else if (x[u] != -INFINITY) {
+        sum += __builtin_amdgcn_exp2f((x[u] - mx) * kLog2e);
+      }
     }
-    L = mx + __builtin_amdgcn_logf(sum) * kLn2;
   }
+  const float L = mx == -INFINITY ? -INFINITY : mx + __builtin_amdgcn_logf(sum) * kLn2;
   float acc[8][8];
 #pragma unroll
   for (int p = 0; p < 8; ++p)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[p][e] = 0.f;
-  if (L != -INFINITY) {
+  if (L != -INFINITY && !nan) {
+    const uint8_t* src0 = (const uint8_t*)a.part_o + (int64_t)base * partial_slot_bytes(a.rows) +
+                          (int64_t)rt * kPartialTileBytes + 8 * 1024 * v + 16 * lane;
     for (int i = 0; i < ns; ++i) {
-      const float x = ok ? a.part_lse[(int64_t)(base + i) * a.rows + row] : -INFINITY;
+      const float x = ok ? lse_p[(int64_t)i * a.rows] : -INFINITY;
       const float wgt = __builtin_amdgcn_exp2f((x - L) * kLog2e);
-      const uint8_t* src = (const uint8_t*)a.part_o + (int64_t)(base + i) * partial_slot_bytes(a.rows) +
-                           (int64_t)rt * kPartialTileBytes + 8 * 1024 * v + 16 * lane;
+      const uint8_t* src = src0 + (int64_t)i * partial_slot_bytes(a.rows);
 #pragma unroll
       for (int p = 0; p < 8; ++p) {
         const bf16x8 pv = *(const bf16x8*)(src + 1024 * p);
@@ -638,8 +669,9 @@ __global__ __launch_bounds__(256) void combine_tiles_kernel(DecodeArgs a) {
       }
     }
   }
+  float Lo = L;
   if (nan) {
-    L = __builtin_nanf("");
+    Lo = __builtin_nanf("");
 #pragma unroll
     for (int p = 0; p < 8; ++p)
 #pragma unroll
@@ -660,7 +692,7 @@ __global__ __launch_bounds__(256) void combine_tiles_kernel(DecodeArgs a) {
   }
   if (v == 0 && h == 0 && ok) {
     const int qi = row / a.h_q, hh = row - qi * a.h_q;
-    a.lse[(int64_t)b * a.l_sb + (int64_t)qi * a.l_ss + (int64_t)hh * a.l_sh] = L;
+    a.lse[(int64_t)b * a.l_sb + (int64_t)qi * a.l_ss + (int64_t)hh * a.l_sh] = Lo;
   }
   __syncthreads();
   // wave v writes rows 8 v .. 8 v + 7, 64 lanes x 16 bytes each
@@ -671,6 +703,144 @@ __global__ __launch_bounds__(256) void combine_tiles_kernel(DecodeArgs a) {
       const int qi = orow / a.h_q, hh = orow - qi * a.h_q;
       uint16_t* op = a.out + (int64_t)b * a.o_sb + (int64_t)qi * a.o_ss + (int64_t)hh * a.o_sh + 8 * lane;
       *(bf16x8*)op = *(const bf16x8*)&tile[jr][8 * lane];
+    }
+  }
+}
+
+// The same merge for sequences split many ways (a few long sequences over
+// many parts).  Workgroup (b, rt, ct) merges column tile ct (32 columns) of
+// row tile rt (32 rows) of sequence b over all its splits:
+//   1. L = log sum_i exp(lse_i) per row, each row's splits spread over eight
+//      threads (online max and sum, four loads in flight), then merged;
+//   2. wave v accumulates splits v, v + 4, ... weighted by exp(lse_i - L),
+//      four splits' loads in flight per lane;
+//   3. the four waves' sums are added through LDS and written as 32 rows of
+//      64 contiguous bytes, lse by the workgroup of column tile 0.
+// A row whose partials are all -inf gets out = 0 and lse = -inf; a NaN
+// partial lse makes the row's out and lse NaN.
+__global__ __launch_bounds__(256) void combine_splits_kernel(DecodeArgs a) {
+  __shared__ float s_m[8][32], s_s[8][32];
+  __shared__ int s_nan[8][32];
+  __shared__ float s_L[32];
+  __shared__ float red[4][64][16];
+  const int b = blockIdx.x, rt = blockIdx.y, ct = blockIdx.z;
+  const int v = threadIdx.x >> 6;
+  const int base = a.num_splits[b];
+  const int ns = a.num_splits[b + 1] - base;
+  if (ns <= 1) return;
+  const int t = threadIdx.x;
+  const float* lse_p = a.part_lse + (int64_t)base * a.rows + 32 * rt;
+  {
+    // 1. this thread's share of row j's splits: i = sub, sub + 8, ...
+    const int j = t & 31, sub = t >> 5;
+    const bool ok = 32 * rt + j < a.rows;
+    float m = -INFINITY, sum = 0.f;
+    bool nan = false;
+    for (int i0 = sub; i0 < ns; i0 += 8 * kMergeUnroll) {
+      float x[kMergeUnroll];
+#pragma unroll
+      for (int u = 0; u < kMergeUnroll; ++u) {
+        const int i = i0 + 8 * u;
+        x[u] = (ok && i < ns) ? lse_p[(int64_t)i * a.rows + j] : -INFINITY;
+      }
+#pragma unroll
+      for (int u = 0; u < kMergeUnroll; ++u) {
+        if (x[u] != x[u]) {
+          nan = true;
+        } else if (x[u] > m) {
+          sum = sum * __builtin_amdgcn_exp2f((m - x[u]) * kLog2e) + 1.f;
+          m = x[u];
+        } else if (x[u] != -INFINITY) {
+          sum += __builtin_amdgcn_exp2f((x[u] - m) * kLog2e);
+        }
+      }
+    }
+    s_m[sub][j] = m;
+    s_s[sub][j] = sum;
+    s_nan[sub][j] = nan;
+  }
+  __syncthreads();
+  if (t < 32) {
+    float m = -INFINITY;
+    bool nan = false;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      m = fmaxf(m, s_m[k][t]);
+      nan |= s_nan[k][t] != 0;
+    }
+    float L = -INFINITY;
+    if (m != -INFINITY) {
+      float sum = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (s_m[k][t] != -INFINITY) sum += s_s[k][t] * __builtin_amdgcn_exp2f((s_m[k][t] - m) * kLog2e);
+      L = m + __builtin_amdgcn_logf(sum) * kLn2;
+    }
+    s_L[t] = nan ? __builtin_nanf("") : L;
+  }
+  __syncthreads();
+  {
+    // 2. wave v: splits v, v + 4, ...
+    const int lane = t & 63, j = lane & 31;
+    const bool ok = 32 * rt + j < a.rows;
+    const float L = s_L[j];
+    float acc[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    if (ok && L != -INFINITY && L == L) {
+      const uint8_t* src0 = (const uint8_t*)a.part_o + (int64_t)base * partial_slot_bytes(a.rows) +
+                            (int64_t)rt * kPartialTileBytes + 2048 * ct + 16 * lane;
+      for (int i0 = v; i0 < ns; i0 += 4 * kMergeUnroll) {
+        float x[kMergeUnroll];
+        bf16x8 d[kMergeUnroll][2];
+#pragma unroll
+        for (int u = 0; u < kMergeUnroll; ++u) {
+          const int i = i0 + 4 * u;
+          if (i < ns) {
+            x[u] = lse_p[(int64_t)i * a.rows + j];
+            const uint8_t* src = src0 + (int64_t)i * partial_slot_bytes(a.rows);
+            d[u][0] = *(const bf16x8*)src;
+            d[u][1] = *(const bf16x8*)(src + 1024);
+          } else {
+            x[u] = -INFINITY;
+            d[u][0] = d[u][1] = bf16x8{};
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kMergeUnroll; ++u) {
+          const float wgt = __builtin_amdgcn_exp2f((x[u] - L) * kLog2e);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            acc[e] += wgt * (float)d[u][0][e];
+            acc[8 + e] += wgt * (float)d[u][1][e];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) red[v][lane][e] = acc[e];
+  }
+  __syncthreads();
+  {
+    // 3. row j = t / 8, output columns 4 c .. 4 c + 3 of the tile; column i
+    // of the tile is accumulator 4 (i / 8) + i % 4 of lane j + 32 ((i / 4) % 2)
+    const int j = t >> 3, c = t & 7;
+    const int row = 32 * rt + j;
+    const float L = s_L[j];
+    bf16x4 o4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * c + e;
+      const int ln = j + 32 * ((i >> 2) & 1), r = 4 * (i >> 3) + (i & 3);
+      float val = red[0][ln][r] + red[1][ln][r] + red[2][ln][r] + red[3][ln][r];
+      if (L != L) val = __builtin_nanf("");
+      o4[e] = (__bf16)val;
+    }
+    if (row < a.rows) {
+      const int qi = row / a.h_q, hh = row - qi * a.h_q;
+      uint16_t* op = a.out + (int64_t)b * a.o_sb + (int64_t)qi * a.o_ss + (int64_t)hh * a.o_sh + 32 * ct + 4 * c;
+      *(bf16x4*)op = o4;
+      if (ct == 0 && c == 0) a.lse[(int64_t)b * a.l_sb + (int64_t)qi * a.l_ss + (int64_t)hh * a.l_sh] = L;
     }
   }
 }
@@ -753,8 +923,16 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
 
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream) {
   if (rows_per_block(a.rows) == kRowsPerWorkgroup) {
-    const dim3 grid((unsigned)a.batch, (unsigned)((a.rows + 31) / 32));
-    hipLaunchKernelGGL(combine_tiles_kernel, grid, dim3(256), 0, stream, a);
+    // many splits per sequence on average (a few long sequences over many
+    // parts): spread each row tile's splits over four waves as well
+    const bool many = (int64_t)a.num_parts + a.batch >= (int64_t)8 * a.batch;
+    if (many) {
+      const dim3 grid((unsigned)a.batch, (unsigned)((a.rows + 31) / 32), (unsigned)(kDv / 32));
+      hipLaunchKernelGGL(combine_splits_kernel, grid, dim3(256), 0, stream, a);
+    } else {
+      const dim3 grid((unsigned)a.batch, (unsigned)((a.rows + 31) / 32));
+      hipLaunchKernelGGL(combine_tiles_kernel, grid, dim3(256), 0, stream, a);
+    }
     return hipGetLastError();
   }
   const dim3 grid((unsigned)a.batch, (unsigned)((a.rows + 3) / 4));

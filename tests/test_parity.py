@@ -109,6 +109,12 @@ SMALL = [
     ((77,), 1, 1, False, 576, 1),
     ((640, 17), 2, 8, True, 576, 9),
     ((129, 300, 64, 5), 1, 256, False, 576, 6),
+    # three and four query tokens (multi-token prediction / speculative decode)
+    ((200, 90, 1), 3, 128, True, 576, 5),
+    ((500, 64), 4, 128, True, 640, 3),
+    ((300, 33, 3), 4, 16, True, 576, 2),
+    ((129, 70), 3, 32, True, 576, None),
+    ((260,), 4, 64, False, 576, 2),
 ]
 
 

@@ -80,3 +80,26 @@ def test_poison_marks_exactly_the_unused_bytes():
             assert torch.isfinite(row).all()
             used_rows += 1
     assert int(torch.isfinite(k[..., 0]).sum()) == used_rows
+
+
+def test_bench_overrides_rename_the_workload():
+    """bench.py's layout/shape overrides change only what they name, and rename the
+    workload so that no counter summary of the plain workload is attached to it."""
+    import sys
+
+    import bench
+    argv = sys.argv
+    try:
+        sys.argv = ["bench.py", "--workload", "wide"]
+        plain = bench.chosen_workload(bench.parse())
+        sys.argv = ["bench.py", "--workload", "wide", "--pitch", "640", "--table", "randperm",
+                    "--seqlen-mean", "2048", "--s-q", "2", "--causal", "yes"]
+        w = bench.chosen_workload(bench.parse())
+    finally:
+        sys.argv = argv
+    assert plain == WORKLOADS["wide"]
+    assert w.name != "wide" and w.name.startswith("wide+")
+    assert (w.pitch, w.table, w.seqlens, w.s_q, w.causal) == (640, "randperm", "normal_2048_512", 2, True)
+    assert (w.batch, w.h_q, w.h_kv) == (plain.batch, plain.h_q, plain.h_kv)
+    s = draw(w).cache_seqlens
+    assert int(s.min()) >= 1 and int(s.max()) <= 4096
