@@ -63,6 +63,9 @@ def parse():
     ap.add_argument("--s-q", type=int, default=None, help="query tokens per sequence")
     ap.add_argument("--h-q", type=int, default=None, help="query heads")
     ap.add_argument("--causal", choices=("yes", "no"), default=None)
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step (plan + decode) in a HIP graph and time its replays "
+                         "(removes the host's launch overhead, which small workloads feel)")
     ap.add_argument("--flush", action="store_true",
                     help="write 512 MB before every timed step so that no input stays in L2 or the "
                          "256 MB Infinity Cache; the step time is then taken from HIP events")
@@ -181,6 +184,20 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    graph = None
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
 
     # timed region: exactly `steps` steps; events bracket the decode call of each
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
@@ -192,6 +209,11 @@ def main():
         if flush is not None:
             flush.fill_(i & 255)
         e0.record()
+        if graph is not None:  # plan and decode in one replay (e1 marks nothing)
+            e1.record()
+            graph.replay()
+            e2.record()
+            continue
         meta = get_mla_metadata(inp.cache_seqlens, rows, w.h_kv, num_parts=parts)
         e1.record()
         mla_decode_with_kvcache(inp.q, inp.blocked_k, inp.block_table, inp.cache_seqlens, D_V,
@@ -231,6 +253,7 @@ def main():
             "batch": b, "s_q": w.s_q, "h_q": w.h_q, "h_kv": w.h_kv, "d": 576, "dv": 512,
             "block_size": 64, "entry_pitch": w.pitch, "block_table": w.table, "causal": w.causal,
             "caches": "flushed before each step" if args.flush else "warm",
+            "launch": "HIP graph replay" if args.graph else "eager",
             "total_seqlens": cost["total_seqlens"], "num_parts": parts,
             "parallelism": "single GPU",
         },
@@ -244,7 +267,8 @@ def main():
                      "decode_p90": round(float(np.percentile(decode_ms, 90)), 5)},
         "roofline": {
             "bound": "hbm",
-            "kernel": "mla_decode_with_kvcache (split-KV decode + lse merge)",
+            "kernel": ("plan + split-KV decode + lse merge (one graph replay)" if args.graph
+                       else "mla_decode_with_kvcache (split-KV decode + lse merge)"),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

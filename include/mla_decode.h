@@ -169,6 +169,40 @@ typedef struct mla_decode_params {
  */
 int mla_decode_with_kvcache(const mla_decode_params* params, void* stream);
 
+/* ---- Writes into the paged cache (the steps before a decode).
+ *
+ * A cache view is (base, num_blocks, block_stride, row_stride) in elements:
+ * row r of page k starts at base + k * block_stride + r * row_stride and its
+ * first 576 elements are the entry.  Rules: base 16-byte aligned, both
+ * strides multiples of 8, row_stride >= 576 (576 dense, 640 for vLLM pull
+ * request "[Perf] Mem align KV caches for CUDA devices (MLA perf
+ * improvement) #12676"'s 256-byte-aligned entries), block_stride >=
+ * 63 * row_stride + 576; otherwise MLA_ERR_BAD_STRIDE.  Elements past the
+ * 576th of a row are never read or written.  All pointers are device
+ * pointers (or host memory the device can access); the caller owns them.
+ *
+ * mla_append_kv: token t's entry (kv_c[t, 0:512] followed by k_pe[t, 0:64],
+ * bf16, rows kv_c_stride / k_pe_stride elements apart, 16-byte aligned) is
+ * written to row slot % 64 of page slot / 64, slot = slot_mapping[t] (int64).
+ * A negative slot (a padding token) or one past num_blocks * 64 is skipped.
+ * Two tokens with the same slot race (precondition: distinct slots).
+ * num_tokens = 0 launches nothing.
+ *
+ * mla_copy_blocks: for each pair k of block_mapping (int64 [num_pairs][2],
+ * device memory), the 64 entries of page mapping[k][0] of the source cache
+ * are copied to page mapping[k][1] of the destination cache.  The two views
+ * may be the same cache (a block copy) or different caches of either pitch
+ * (a swap or re-layout).  A pair naming a page outside its pool is skipped.
+ * Pairs must not write a page another pair of the same call reads or writes.
+ */
+int mla_append_kv(const void* kv_c, int64_t kv_c_stride, const void* k_pe, int64_t k_pe_stride,
+                  const int64_t* slot_mapping, int32_t num_tokens, void* k_cache, int32_t num_blocks,
+                  int64_t k_block_stride, int64_t k_row_stride, void* stream);
+
+int mla_copy_blocks(const void* src_cache, int32_t src_num_blocks, int64_t src_block_stride,
+                    int64_t src_row_stride, void* dst_cache, int32_t dst_num_blocks, int64_t dst_block_stride,
+                    int64_t dst_row_stride, const int64_t* block_mapping, int32_t num_pairs, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,7 +26,7 @@ from . import _lib
 from ._lib import MLAError, TILE_MD_INTS
 
 __all__ = ["get_mla_metadata", "mla_decode_with_kvcache", "plan_host", "default_num_parts",
-           "workspace_size", "MLAError", "TILE_MD_INTS"]
+           "workspace_size", "append_kv", "copy_blocks", "MLAError", "TILE_MD_INTS"]
 
 D_QK = 576
 D_V = 512
@@ -161,3 +161,61 @@ def mla_decode_with_kvcache(q: torch.Tensor, blocked_k: torch.Tensor, block_tabl
     _lib.check(_lib.load().mla_decode_with_kvcache(ctypes.byref(p), _stream(dev)),
                "mla_decode_with_kvcache")
     return out, lse
+
+
+def _cache_view(blocked_k: torch.Tensor, what: str):
+    """(num_blocks, block_stride, row_stride) of a [num_blocks, 64, 1, 576] bf16 cache view."""
+    if blocked_k.dim() != 4 or tuple(blocked_k.shape[1:]) != (BLOCK_SIZE, 1, D_QK):
+        raise ValueError(f"{what} must be [num_blocks, 64, 1, 576]")
+    if blocked_k.dtype != torch.bfloat16 or not blocked_k.is_cuda or blocked_k.stride(-1) != 1:
+        raise ValueError(f"{what} must be a bf16 GPU tensor with a contiguous last dimension")
+    return blocked_k.shape[0], blocked_k.stride(0), blocked_k.stride(1)
+
+
+def append_kv(kv_c: torch.Tensor, k_pe: torch.Tensor, slot_mapping: torch.Tensor,
+              blocked_k: torch.Tensor) -> None:
+    """Write token t's entry (kv_c[t] then k_pe[t]) to cache slot slot_mapping[t].
+
+    kv_c bf16 [T, 512], k_pe bf16 [T, 64] (rows may be strided), slot_mapping
+    int64 [T] (negative = skip), blocked_k the cache view the decode reads
+    ([num_blocks, 64, 1, 576], either entry pitch).  Enqueued on the current
+    stream.
+    """
+    if kv_c.dim() != 2 or kv_c.shape[1] != D_V or k_pe.dim() != 2 or k_pe.shape[1] != D_QK - D_V:
+        raise ValueError("kv_c must be [T, 512] and k_pe [T, 64]")
+    if kv_c.dtype != torch.bfloat16 or k_pe.dtype != torch.bfloat16:
+        raise ValueError("kv_c and k_pe must be bfloat16")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.dim() != 1:
+        raise ValueError("slot_mapping must be a 1-D int64 tensor")
+    t = kv_c.shape[0]
+    if k_pe.shape[0] != t or slot_mapping.numel() != t:
+        raise ValueError("kv_c, k_pe and slot_mapping disagree on the token count")
+    dev = blocked_k.device
+    for x in (kv_c, k_pe, slot_mapping):
+        if not x.is_cuda or x.device != dev:
+            raise ValueError("all tensors must be on the cache's GPU")
+    if kv_c.stride(1) != 1 or k_pe.stride(1) != 1:
+        raise ValueError("kv_c and k_pe rows must be contiguous")
+    nb, bs, rs = _cache_view(blocked_k, "blocked_k")
+    slots = slot_mapping.contiguous()
+    _lib.check(_lib.load().mla_append_kv(_ptr(kv_c), kv_c.stride(0), _ptr(k_pe), k_pe.stride(0), _ptr(slots),
+                                         t, _ptr(blocked_k), nb, bs, rs, _stream(dev)), "mla_append_kv")
+
+
+def copy_blocks(src_k: torch.Tensor, dst_k: torch.Tensor, block_mapping: torch.Tensor) -> None:
+    """Copy page block_mapping[k, 0] of src_k to page block_mapping[k, 1] of dst_k, for every k.
+
+    src_k and dst_k are cache views ([num_blocks, 64, 1, 576], either entry
+    pitch; the same tensor for an in-place block copy); block_mapping is int64
+    [num_pairs, 2] on the GPU.  Enqueued on the current stream.
+    """
+    if block_mapping.dtype != torch.int64 or block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be an int64 [num_pairs, 2] tensor")
+    dev = dst_k.device
+    if src_k.device != dev or block_mapping.device != dev:
+        raise ValueError("all tensors must be on the same GPU")
+    sn, sbs, srs = _cache_view(src_k, "src_k")
+    dn, dbs, drs = _cache_view(dst_k, "dst_k")
+    m = block_mapping.contiguous()
+    _lib.check(_lib.load().mla_copy_blocks(_ptr(src_k), sn, sbs, srs, _ptr(dst_k), dn, dbs, drs, _ptr(m),
+                                           m.shape[0], _stream(dev)), "mla_copy_blocks")

@@ -33,6 +33,8 @@ EXPORTS = (
     "mla_plan_host",
     "mla_workspace_size",
     "mla_decode_with_kvcache",
+    "mla_append_kv",
+    "mla_copy_blocks",
 )
 
 c_i32 = ctypes.c_int32
@@ -95,6 +97,10 @@ def load():
                                            ctypes.POINTER(ctypes.c_size_t)]
         lib.mla_decode_with_kvcache.restype = ctypes.c_int
         lib.mla_decode_with_kvcache.argtypes = [ctypes.POINTER(DecodeParams), c_p]
+        lib.mla_append_kv.restype = ctypes.c_int
+        lib.mla_append_kv.argtypes = [c_p, c_i64, c_p, c_i64, c_p, c_i32, c_p, c_i32, c_i64, c_i64, c_p]
+        lib.mla_copy_blocks.restype = ctypes.c_int
+        lib.mla_copy_blocks.argtypes = [c_p, c_i32, c_i64, c_i64, c_p, c_i32, c_i64, c_i64, c_p, c_i32, c_p]
         if lib.mla_decode_params_size() != ctypes.sizeof(DecodeParams):
             raise RuntimeError("mla_decode_params layout mismatch between the binding and the library")
         _lib = lib

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_NAME = "libmla_decode.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["mla_api.hip", "mla_kernels.hip", "mla_decode_wide.hip"]
+SOURCES = ["mla_api.hip", "mla_kernels.hip", "mla_decode_wide.hip", "mla_cache.hip"]
 ARCH = os.environ.get("MLA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

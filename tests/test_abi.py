@@ -155,3 +155,58 @@ def test_workspace_size_formula(lib):
         assert n.value == want
     assert lib.mla_workspace_size(2, 1, 16, 1, 512, 4, None) == _lib.MLA_ERR_NULL_POINTER
     assert lib.mla_workspace_size(2, 0, 16, 1, 512, 4, ctypes.byref(n)) == _lib.MLA_ERR_BAD_SHAPE
+
+
+def append_args(**over):
+    vals = dict(kv_c=FAKE, kv_c_stride=512, k_pe=FAKE, k_pe_stride=64, slots=FAKE, num_tokens=4, cache=FAKE,
+                num_blocks=8, block_stride=64 * 640, row_stride=640, stream=None)
+    vals.update(over)
+    return [vals[k] for k in ("kv_c", "kv_c_stride", "k_pe", "k_pe_stride", "slots", "num_tokens", "cache",
+                              "num_blocks", "block_stride", "row_stride", "stream")]
+
+
+APPEND_BAD = [
+    ("null kv_c", dict(kv_c=None), _lib.MLA_ERR_NULL_POINTER),
+    ("null k_pe", dict(k_pe=None), _lib.MLA_ERR_NULL_POINTER),
+    ("null slots", dict(slots=None), _lib.MLA_ERR_NULL_POINTER),
+    ("null cache", dict(cache=None), _lib.MLA_ERR_NULL_POINTER),
+    ("negative tokens", dict(num_tokens=-1), _lib.MLA_ERR_BAD_SHAPE),
+    ("negative blocks", dict(num_blocks=-1), _lib.MLA_ERR_BAD_SHAPE),
+    ("misaligned cache", dict(cache=FAKE + 8), _lib.MLA_ERR_BAD_STRIDE),
+    ("misaligned kv_c", dict(kv_c=FAKE + 2), _lib.MLA_ERR_BAD_STRIDE),
+    ("short kv_c rows", dict(kv_c_stride=504), _lib.MLA_ERR_BAD_STRIDE),
+    ("odd k_pe rows", dict(k_pe_stride=68), _lib.MLA_ERR_BAD_STRIDE),
+    ("pitch < 576", dict(row_stride=568, block_stride=64 * 568), _lib.MLA_ERR_BAD_STRIDE),
+    ("odd pitch", dict(row_stride=580, block_stride=64 * 580), _lib.MLA_ERR_BAD_STRIDE),
+    ("pages overlap", dict(block_stride=63 * 640), _lib.MLA_ERR_BAD_STRIDE),
+]
+
+
+@pytest.mark.parametrize("name,over,status", APPEND_BAD, ids=[b[0] for b in APPEND_BAD])
+def test_append_rejects_bad_arguments(lib, name, over, status):
+    assert lib.mla_append_kv(*append_args(**over)) == status
+
+
+def test_append_of_no_tokens_is_a_no_op(lib):
+    assert lib.mla_append_kv(*append_args(num_tokens=0, kv_c=None, cache=None)) == _lib.MLA_OK
+
+
+def test_copy_blocks_rejects_bad_arguments(lib):
+    f = lib.mla_copy_blocks
+    ok = (FAKE, 8, 64 * 576, 576, FAKE, 8, 64 * 640, 640, FAKE, 2, None)
+
+    def call(**over):
+        names = ("src", "sn", "sbs", "srs", "dst", "dn", "dbs", "drs", "map", "pairs", "stream")
+        args = dict(zip(names, ok))
+        args.update(over)
+        return f(*[args[n] for n in names])
+
+    assert call(src=None) == _lib.MLA_ERR_NULL_POINTER
+    assert call(dst=None) == _lib.MLA_ERR_NULL_POINTER
+    assert call(map=None) == _lib.MLA_ERR_NULL_POINTER
+    assert call(pairs=-1) == _lib.MLA_ERR_BAD_SHAPE
+    assert call(pairs=0, src=None, map=None) == _lib.MLA_OK
+    assert call(sn=-2) == _lib.MLA_ERR_BAD_SHAPE
+    assert call(srs=570) == _lib.MLA_ERR_BAD_STRIDE
+    assert call(dbs=63 * 640) == _lib.MLA_ERR_BAD_STRIDE
+    assert call(dst=FAKE + 4) == _lib.MLA_ERR_BAD_STRIDE
