@@ -109,25 +109,32 @@ __device__ __forceinline__ void score_mfma2(f32x16& s, bf16x8 k0, bf16x8 k1, bf1
 // ct, touched only by the assembly below (the compiler never holds them, so
 // it cannot copy or spill them; the zeroing names every one of them as
 // clobbered, which reserves all 256 for the kernel).
-// Two value MFMAs, tiles CT and CT + 1 (CT even), in one statement: one wait
-// for both operands.
-#define MLA_VMFMA2(L0, H0, L1, H1)                                                                  \
-  asm volatile("v_mfma_f32_32x32x16_bf16 a[" #L0 ":" #H0 "], %0, %2, a[" #L0 ":" #H0 "]\n\t"           \
-               "v_mfma_f32_32x32x16_bf16 a[" #L1 ":" #H1 "], %1, %2, a[" #L1 ":" #H1 "]" ::"v"(v0), \
-               "v"(v1), "v"(p))
+// One value MFMA, tile CT, per statement: the softmax's VALU work goes between
+// consecutive MFMAs, where it runs while the matrix core works (VALU work
+// issued after two back-to-back MFMAs waits for them instead).
+#define MLA_VMFMA1(L, H) \
+  asm volatile("v_mfma_f32_32x32x16_bf16 a[" #L ":" #H "], %0, %1, a[" #L ":" #H "]" ::"v"(v), "v"(p))
 template <int CT>
-__device__ __forceinline__ void value_mfma2(bf16x8 v0, bf16x8 v1, bf16x8 p) {
-  static_assert(CT % 2 == 0 && CT < 16, "tile pair");
-  if constexpr (CT == 0) MLA_VMFMA2(0, 15, 16, 31);
-  else if constexpr (CT == 2) MLA_VMFMA2(32, 47, 48, 63);
-  else if constexpr (CT == 4) MLA_VMFMA2(64, 79, 80, 95);
-  else if constexpr (CT == 6) MLA_VMFMA2(96, 111, 112, 127);
-  else if constexpr (CT == 8) MLA_VMFMA2(128, 143, 144, 159);
-  else if constexpr (CT == 10) MLA_VMFMA2(160, 175, 176, 191);
-  else if constexpr (CT == 12) MLA_VMFMA2(192, 207, 208, 223);
-  else if constexpr (CT == 14) MLA_VMFMA2(224, 239, 240, 255);
+__device__ __forceinline__ void value_mfma1(bf16x8 v, bf16x8 p) {
+  static_assert(CT >= 0 && CT < 16, "tile");
+  if constexpr (CT == 0) MLA_VMFMA1(0, 15);
+  else if constexpr (CT == 1) MLA_VMFMA1(16, 31);
+  else if constexpr (CT == 2) MLA_VMFMA1(32, 47);
+  else if constexpr (CT == 3) MLA_VMFMA1(48, 63);
+  else if constexpr (CT == 4) MLA_VMFMA1(64, 79);
+  else if constexpr (CT == 5) MLA_VMFMA1(80, 95);
+  else if constexpr (CT == 6) MLA_VMFMA1(96, 111);
+  else if constexpr (CT == 7) MLA_VMFMA1(112, 127);
+  else if constexpr (CT == 8) MLA_VMFMA1(128, 143);
+  else if constexpr (CT == 9) MLA_VMFMA1(144, 159);
+  else if constexpr (CT == 10) MLA_VMFMA1(160, 175);
+  else if constexpr (CT == 11) MLA_VMFMA1(176, 191);
+  else if constexpr (CT == 12) MLA_VMFMA1(192, 207);
+  else if constexpr (CT == 13) MLA_VMFMA1(208, 223);
+  else if constexpr (CT == 14) MLA_VMFMA1(224, 239);
+  else MLA_VMFMA1(240, 255);
 }
-#undef MLA_VMFMA2
+#undef MLA_VMFMA1
 
 #define MLA_AREAD4(A, B, C, D)                                                                 \
   asm volatile("v_accvgpr_read_b32 %0, a" #A "\n\tv_accvgpr_read_b32 %1, a" #B                  \
@@ -494,7 +501,7 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
   };
 
   // ---- softmax of the scored chunk D (scores in s), in 32 pieces; piece q
-  // runs after value MFMA q when interleaved
+  // runs between value MFMAs q and q + 1 when interleaved
   float mu = 0.f;
   // (FAST: a full chunk inside its segment that no row's limit reaches:
   // no masking and no segment results)
@@ -595,15 +602,11 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
 #pragma unroll
     for (int f = 0; f < kVAhead; ++f) vf[f] = vfrag(f);
     __builtin_amdgcn_sched_barrier(0);
-    static_for<0, kColTiles>([&](auto gc) {
-      constexpr int f = 2 * decltype(gc)::value;  // fragments f, f + 1: tiles f & 15, (f & 15) + 1 of k-step f >> 4
+    static_for<0, 2 * kColTiles>([&](auto fc) {
+      constexpr int f = decltype(fc)::value;  // fragment f: tile f & 15 of k-step f >> 4
       if constexpr (f + kVAhead < 2 * kColTiles) vf[(f + kVAhead) % R] = vfrag(f + kVAhead);
-      if constexpr (f + 1 + kVAhead < 2 * kColTiles) vf[(f + 1 + kVAhead) % R] = vfrag(f + 1 + kVAhead);
-      value_mfma2<(f & 15)>(vf[f % R], vf[(f + 1) % R], pc[f >> 4]);
-      if constexpr (WS != 0) {
-        smax_piece(std::integral_constant<int, f>{}, D, fast_tag);
-        smax_piece(std::integral_constant<int, f + 1>{}, D, fast_tag);
-      }
+      value_mfma1<(f & 15)>(vf[f % R], pc[f >> 4]);
+      if constexpr (WS != 0) smax_piece(std::integral_constant<int, f>{}, D, fast_tag);
       __builtin_amdgcn_sched_barrier(0);
     });
   };
