@@ -90,19 +90,16 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
-// s (+)= K . Q^T for two 16-column steps of d; the accumulator stays in VGPRs
+// s (+)= K . Q^T for one 16-column step of d; the accumulator stays in VGPRs
 // (written as assembly: the compiler would put every MFMA result of the
-// kernel in the register file the value accumulators fill).  Two MFMAs per
-// statement: one wait for the operands of both.
-__device__ __forceinline__ void score_mfma2(f32x16& s, bf16x8 k0, bf16x8 k1, bf16x8 q0, bf16x8 q1, bool first) {
+// kernel in the register file the value accumulators fill).  One MFMA per
+// statement, so that the copies' address work between them overlaps the
+// matrix core.
+__device__ __forceinline__ void score_mfma1(f32x16& s, bf16x8 k, bf16x8 q, bool first) {
   if (first)
-    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %3, 0\n\tv_mfma_f32_32x32x16_bf16 %0, %2, %4, %0"
-        : "=&v"(s)
-        : "v"(k0), "v"(k1), "v"(q0), "v"(q1));
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(k), "v"(q));
   else
-    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %3, %0\n\tv_mfma_f32_32x32x16_bf16 %0, %2, %4, %0"
-        : "+v"(s)
-        : "v"(k0), "v"(k1), "v"(q0), "v"(q1));
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(k), "v"(q));
 }
 
 // ---- the output accumulators: fixed AGPRs, a[16 ct .. 16 ct + 15] for tile
@@ -483,19 +480,18 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
 #pragma unroll
     for (int u = 0; u < 4; ++u) kb[u] = launder(lds + slot_off + (k_lane ^ (32u * u)));
     auto kfrag = [&](int ks) -> bf16x8 { return *(const lds_bf16x8*)(kb[ks & 3] + 4096u * (ks >> 2)); };
-    constexpr int R = kKAhead + 2;  // the reads of a pair go ahead of the pair's MFMAs
+    constexpr int R = kKAhead + 2;  // the read of step k goes ahead of MFMA k
     bf16x8 kf[R];
 #pragma unroll
     for (int ks = 0; ks < kKAhead; ++ks) kf[ks] = kfrag(ks);
     __amdgpu_buffer_rsrc_t rsrc;
     if constexpr (WC) rsrc = copy_rsrc(cc);
     __builtin_amdgcn_sched_barrier(0);
-    static_for<0, kSSteps / 2>([&](auto pc_) {
-      constexpr int k0 = 2 * decltype(pc_)::value;
-      if constexpr (k0 + kKAhead < kSSteps) kf[(k0 + kKAhead) % R] = kfrag(k0 + kKAhead);
-      if constexpr (k0 + 1 + kKAhead < kSSteps) kf[(k0 + 1 + kKAhead) % R] = kfrag(k0 + 1 + kKAhead);
-      score_mfma2(s, kf[k0 % R], kf[(k0 + 1) % R], qf[k0], qf[k0 + 1], k0 == 0);
-      if constexpr (WC && k0 % 4 == 0) copy_one(rsrc, cc_slot, std::integral_constant<int, k0 / 4>{});
+    static_for<0, kSSteps>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      if constexpr (k + kKAhead < kSSteps) kf[(k + kKAhead) % R] = kfrag(k + kKAhead);
+      score_mfma1(s, kf[k % R], qf[k], k == 0);
+      if constexpr (WC && k % 4 == 1) copy_one(rsrc, cc_slot, std::integral_constant<int, k / 4>{});
       __builtin_amdgcn_sched_barrier(0);
     });
   };
