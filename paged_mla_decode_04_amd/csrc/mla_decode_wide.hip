@@ -56,8 +56,8 @@ constexpr int kSmemW = kSlots * kTileBytes;       // 147456
 constexpr int kSSteps = kD / 16;                  // 36 score k-steps
 constexpr int kColTiles = kDv / 32;               // 16 output column tiles
 constexpr int kCopiesW = 9;                       // 1 KB copies per wave per chunk
-constexpr int kKAhead = 6;                        // score K fragments in flight
-constexpr int kVAhead = 6;                        // value V^T fragments in flight
+constexpr int kKAhead = 4;                        // score K fragments in flight
+constexpr int kVAhead = 8;                        // value V^T fragments in flight
 static_assert(kSmemW <= 160 * 1024, "LDS budget");
 static_assert(kThreadsW / 64 * kCopiesW * 1024 == kTileBytes, "copies cover the chunk");
 
