@@ -124,6 +124,13 @@ def test_decode_rejects_null_params(lib):
     assert lib.mla_decode_with_kvcache(None, None) == _lib.MLA_ERR_NULL_POINTER
 
 
+def test_batch_past_the_device_plan_needs_metadata(lib):
+    # without metadata the library plans on the device, which holds at most
+    # 16384 sequences; with metadata any batch is accepted
+    p = good_params(batch=16385, tile_md=None, num_splits=None, num_parts=4)
+    assert lib.mla_decode_with_kvcache(ctypes.byref(p), None) == _lib.MLA_ERR_UNSUPPORTED
+
+
 def test_empty_batch_is_a_no_op(lib):
     p = good_params(batch=0, q=None, out=None)
     assert lib.mla_decode_with_kvcache(ctypes.byref(p), None) == _lib.MLA_OK

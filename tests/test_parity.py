@@ -233,3 +233,30 @@ def test_growing_scores_exercise_the_rescale(h_q, s_q, causal, parts):
     ref_out, ref_lse = oracle(inp)
     assert float(ref_lse.max()) > 40.0  # far past several rescale thresholds
     assert_parity(out, lse, ref_out, ref_lse, what="ramp")
+
+
+def test_maximum_rows():
+    """s_q * h_q at the library's limit (1024 rows: eight row blocks), causal."""
+    w = Workload("maxrows", batch=3, s_q=8, h_q=128, causal=True, seqlens="fixed",
+                 fixed_seqlens=(70, 9, 200))
+    inp = draw(w, seed=21, poison=True)
+    note("[parity] maximum rows s_q=8 h_q=128")
+    out, lse, _ = run_gpu(inp, num_parts=5)
+    ref_out, ref_lse = oracle(inp)
+    assert_parity(out, lse, ref_out, ref_lse, what="max rows")
+
+
+def test_large_batch_of_short_sequences():
+    """2048 sequences of 1..300 tokens in one call (many parts touch several
+    sequences each); sampled sequences against the oracle, all rows finite."""
+    rng = np.random.default_rng(5)
+    lens = tuple(int(x) for x in rng.integers(1, 301, size=2048))
+    w = Workload("batch", batch=len(lens), s_q=1, h_q=16, causal=False, seqlens="fixed",
+                 fixed_seqlens=lens)
+    inp = draw(w, seed=22)
+    note("[parity] 2048 short sequences")
+    out, lse, _ = run_gpu(inp)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    seqs = sorted({0, 1, 2047, int(np.argmax(lens)), int(np.argmin(lens))} | set(rng.integers(0, 2048, 8).tolist()))
+    ref_out, ref_lse = oracle(inp, seqs)
+    assert_parity(out, lse, ref_out, ref_lse, rows=seqs, what="large batch")
