@@ -260,3 +260,22 @@ def test_large_batch_of_short_sequences():
     seqs = sorted({0, 1, 2047, int(np.argmax(lens)), int(np.argmin(lens))} | set(rng.integers(0, 2048, 8).tolist()))
     ref_out, ref_lse = oracle(inp, seqs)
     assert_parity(out, lse, ref_out, ref_lse, rows=seqs, what="large batch")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes(seed):
+    """Seeded random shapes: odd head counts (rows not a multiple of 16 or 32),
+    one to four query tokens, both pitches, random part counts, poisoned cache."""
+    from paged_mla_decode_04_amd.workloads import random_case
+    g = torch.Generator().manual_seed(1000 + seed)
+    w = random_case(g, max_batch=4, s_q_choices=(1, 2, 3, 4),
+                    h_q_choices=(1, 3, 8, 16, 24, 48, 64, 96, 128, 160, 256), max_len=700)
+    if w.s_q * w.h_q > 1024:
+        w = Workload(**{**w.__dict__, "s_q": 1})
+    parts = int(torch.randint(1, 65, (1,), generator=g))
+    inp = draw(w, seed=seed, poison=True)
+    note(f"[parity] random seed={seed}: b={w.batch} s_q={w.s_q} h_q={w.h_q} causal={w.causal} "
+         f"pitch={w.pitch} lens={w.fixed_seqlens} parts={parts}")
+    out, lse, _ = run_gpu(inp, num_parts=parts)
+    ref_out, ref_lse = oracle(inp)
+    assert_parity(out, lse, ref_out, ref_lse, what=f"random {seed}")
