@@ -491,7 +491,9 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
       constexpr int k = decltype(kc)::value;
       if constexpr (k + kKAhead < kSSteps) kf[(k + kKAhead) % R] = kfrag(k + kKAhead);
       score_mfma1(s, kf[k % R], qf[k], k == 0);
-      if constexpr (WC && k % 4 == 1) copy_one(rsrc, cc_slot, std::integral_constant<int, k / 4>{});
+      // the copies go out over the first half of the score product (each one as
+      // early as the MFMAs allow, so more of the chunk is in flight)
+      if constexpr (WC && k % 2 == 1 && k < 2 * kCopiesW) copy_one(rsrc, cc_slot, std::integral_constant<int, k / 2>{});
       __builtin_amdgcn_sched_barrier(0);
     });
   };
