@@ -66,9 +66,12 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="capture one step (plan + decode) in a HIP graph and time its replays "
                          "(removes the host's launch overhead, which small workloads feel)")
-    ap.add_argument("--flush", action="store_true",
-                    help="write 512 MB before every timed step so that no input stays in L2 or the "
-                         "256 MB Infinity Cache; the step time is then taken from HIP events")
+    ap.add_argument("--warm", action="store_true",
+                    help="time the steps back to back with warm caches only (by default every "
+                         "timed step is preceded by a 512 MB read of another buffer, outside the "
+                         "step's events, so that no input stays in L2 or the 256 MB Infinity "
+                         "Cache; warm steps are then timed as well and reported beside the cold "
+                         "ones)")
     return ap.parse_args()
 
 
@@ -111,6 +114,29 @@ def copy_probe():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 3}))
+
+
+def copy_bandwidth(dev, nbytes: int = 1 << 30, reps: int = 10) -> dict:
+    """Measured HBM bandwidth of a plain device copy (bytes read + written per second).
+
+    A reference beside the 8 TB/s peak: what streaming reads and writes reach
+    on this GPU with torch's copy kernel, timed with HIP events.
+    """
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return {"value": round(metrics.gbps(2 * nbytes, ms), 1), "unit": "GB/s",
+            "what": f"device copy of {nbytes >> 20} MiB (read + write bytes), mean of {reps}"}
 
 
 def cpu_baseline(inp, budget_s: float):
@@ -199,40 +225,59 @@ def main():
             graph.replay()
         torch.cuda.synchronize()
 
-    # timed region: exactly `steps` steps; events bracket the decode call of each
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    flush = torch.empty((512 << 20,), dtype=torch.uint8, device=dev) if args.flush else None
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i, (e0, e1, e2) in enumerate(ev):
-        if flush is not None:
-            flush.fill_(i & 255)
-        e0.record()
-        if graph is not None:  # plan and decode in one replay (e1 marks nothing)
+    def timed(n_steps: int, flush):
+        """n_steps steps with events around the plan and the decode call of each."""
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True)) for _ in range(n_steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i, (e0, e1, e2) in enumerate(ev):
+            if flush is not None:
+                flush.sum()  # reads 512 MB: L2 and MALL then hold clean lines of another buffer
+            e0.record()
+            if graph is not None:  # plan and decode in one replay (e1 marks nothing)
+                e1.record()
+                graph.replay()
+                e2.record()
+                continue
+            meta = get_mla_metadata(inp.cache_seqlens, rows, w.h_kv, num_parts=parts)
             e1.record()
-            graph.replay()
+            mla_decode_with_kvcache(inp.q, inp.blocked_k, inp.block_table, inp.cache_seqlens, D_V,
+                                    w.softmax_scale, w.causal, metadata=meta, out=out, lse=lse,
+                                    workspace=ws)
             e2.record()
-            continue
-        meta = get_mla_metadata(inp.cache_seqlens, rows, w.h_kv, num_parts=parts)
-        e1.record()
-        mla_decode_with_kvcache(inp.q, inp.blocked_k, inp.block_table, inp.cache_seqlens, D_V,
-                                w.softmax_scale, w.causal, metadata=meta, out=out, lse=lse,
-                                workspace=ws)
-        e2.record()
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3
-    ms_per_step = wall_ms / args.steps
-    if flush is not None:  # the flush is not part of a step
-        ms_per_step = float(np.mean([a.elapsed_time(c) for a, _, c in ev]))
-    plan_ms = float(np.mean([a.elapsed_time(b_) for a, b_, _ in ev]))
-    decode_ms = np.array([b_.elapsed_time(c) for _, b_, c in ev])
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3
+        step_ms = np.array([a.elapsed_time(c) for a, _, c in ev])
+        plan_ms = np.array([a.elapsed_time(b_) for a, b_, _ in ev])
+        decode_ms = np.array([b_.elapsed_time(c) for _, b_, c in ev])
+        # with a flush between steps the step time comes from the events (the
+        # flush is not part of a step); back to back, from the wall clock
+        per_step = float(step_ms.mean()) if flush is not None else wall_ms / n_steps
+        return {"ms_per_step": per_step, "plan_ms": float(plan_ms.mean()),
+                "decode_ms": float(decode_ms.mean()), "decode_median": float(np.median(decode_ms)),
+                "decode_p10": float(np.percentile(decode_ms, 10)),
+                "decode_p90": float(np.percentile(decode_ms, 90))}
+
+    # timed region: exactly `steps` steps (cold: a 512 MB write before each,
+    # outside its events), then, unless --warm made the warm steps the official
+    # ones, the same number of warm steps back to back for reference
+    cold = not args.warm
+    # a read, not a write: written lines would stay dirty in the caches and be
+    # written back to HBM while the next step runs
+    flush = torch.ones((128 << 20,), dtype=torch.float32, device=dev) if cold else None
+    main_t = timed(args.steps, flush)
+    warm_t = timed(args.steps, None) if cold else None
+    if flush is not None:
+        del flush
+    ms_per_step = main_t["ms_per_step"]
+    plan_ms = main_t["plan_ms"]
+    dec_avg = main_t["decode_ms"]
 
     seqlens = inp_host.cache_seqlens
     cost = metrics.workload_cost(seqlens.tolist(), b, w.s_q, w.h_q, w.h_kv)
     gbs = metrics.gbps(cost["bytes"], ms_per_step)
     tfl = metrics.tflops(cost["flops"], ms_per_step)
-    dec_avg = float(decode_ms.mean())
     achieved = metrics.gbps(cost["bytes"], dec_avg)
 
     line = {
@@ -252,7 +297,7 @@ def main():
             "workload": f"{w.name}: {w.description}",
             "batch": b, "s_q": w.s_q, "h_q": w.h_q, "h_kv": w.h_kv, "d": 576, "dv": 512,
             "block_size": 64, "entry_pitch": w.pitch, "block_table": w.table, "causal": w.causal,
-            "caches": "flushed before each step" if args.flush else "warm",
+            "caches": "flushed before each step" if cold else "warm",
             "launch": "HIP graph replay" if args.graph else "eager",
             "total_seqlens": cost["total_seqlens"], "num_parts": parts,
             "parallelism": "single GPU",
@@ -263,8 +308,9 @@ def main():
         "algorithmic_bytes": cost["bytes"],
         "algorithmic_flops": cost["flops"],
         "stage_ms": {"plan": round(plan_ms, 5), "decode_and_merge": round(dec_avg, 5),
-                     "decode_p10": round(float(np.percentile(decode_ms, 10)), 5),
-                     "decode_p90": round(float(np.percentile(decode_ms, 90)), 5)},
+                     "decode_median": round(main_t["decode_median"], 5),
+                     "decode_p10": round(main_t["decode_p10"], 5),
+                     "decode_p90": round(main_t["decode_p90"], 5)},
         "roofline": {
             "bound": "hbm",
             "kernel": ("plan + split-KV decode + lse merge (one graph replay)" if args.graph
@@ -276,6 +322,13 @@ def main():
             "traffic": None,
         },
     }
+    if warm_t is not None:
+        line["warm"] = {"value": round(metrics.gbps(cost["bytes"], warm_t["ms_per_step"]), 2),
+                        "unit": "GB/s", "ms_per_step": round(warm_t["ms_per_step"], 5),
+                        "decode_and_merge_ms": round(warm_t["decode_ms"], 5),
+                        "steps": args.steps}
+    line["copy_bandwidth"] = copy_bandwidth(dev)
+    line["roofline"]["frac_of_copy"] = round(achieved / line["copy_bandwidth"]["value"], 4)
     # measured HBM bytes per decode call (FETCH_SIZE + WRITE_SIZE, copy-calibrated),
     # only when the counters were taken on the current kernel sources
     tr = traffic.load(w.name)

@@ -20,9 +20,13 @@
  *
  * The work is split along the key length and the pieces merged by their lse
  * (Flash-Decoding, as the Hacker News discussion of the FlashMLA release
- * describes it).  The tutorial names the two calls a serving engine makes:
- * metadata preparation once per decode step, and the forward once per layer;
- * mla_get_metadata and mla_decode_with_kvcache follow that split.
+ * describes it).  The same tutorial, section 二.2 (FlashMLA as a vLLM
+ * attention backend), names the two calls a serving engine makes: a metadata
+ * builder prepares the forward's metadata with get_mla_metadata, and the
+ * attention implementation runs the forward with flash_mla_with_kvcache.
+ * mla_get_metadata and mla_decode_with_kvcache follow that split; since the
+ * plan depends only on the lengths, one plan serves every layer of a step
+ * (our reading).
  *
  * Cache entries may be stored at the dense 576-element pitch or at the
  * 256-byte-aligned 640-element pitch of vLLM pull request "[Perf] Mem align
@@ -72,7 +76,7 @@ typedef enum mla_status {
 #define MLA_MAX_ROWS 1024
 
 /* Static, NUL-terminated description of a status. */
-const char* mla_status_string(int status);
+const char* mla_status_string(mla_status status);
 
 /* sizeof(mla_decode_params) as compiled into the library, so that foreign-language
    bindings can check their mirror of the struct. */
@@ -83,7 +87,7 @@ size_t mla_decode_params_size(void);
  * q_rows = s_q * h_q query rows over h_kv kv heads: one workgroup per compute
  * unit, shared among the row blocks.  Advisory; any value >= 1 is valid.
  */
-int mla_default_num_parts(int device, int32_t q_rows, int32_t h_kv, int32_t* num_parts);
+mla_status mla_default_num_parts(int device, int32_t q_rows, int32_t h_kv, int32_t* num_parts);
 
 /*
  * The split-KV plan (tile-scheduler metadata), enqueued on `stream`.
@@ -101,21 +105,21 @@ int mla_default_num_parts(int device, int32_t q_rows, int32_t h_kv, int32_t* num
  * The plan depends only on (cache_seqlens, batch, q_rows, h_kv, num_parts), so one plan
  * serves every layer's decode of one step.  Asynchronous; the caller owns all buffers.
  */
-int mla_get_metadata(const int32_t* cache_seqlens_d, int32_t batch, int32_t q_rows,
+mla_status mla_get_metadata(const int32_t* cache_seqlens_d, int32_t batch, int32_t q_rows,
                      int32_t h_kv, int32_t num_parts, int32_t* tile_md_d,
                      int32_t* num_splits_d, void* stream);
 
 /* The same plan computed on the host from host arrays; bit-identical to mla_get_metadata. */
-int mla_plan_host(const int32_t* cache_seqlens_h, int32_t batch, int32_t q_rows, int32_t h_kv,
+mla_status mla_plan_host(const int32_t* cache_seqlens_h, int32_t batch, int32_t q_rows, int32_t h_kv,
                   int32_t num_parts, int32_t* tile_md_h, int32_t* num_splits_h);
 
 /*
  * Workspace bytes mla_decode_with_kvcache needs for these sizes: room for an internal
  * plan (used when no plan is passed) and for the per-split partial results
- * ((batch + num_parts) slots of rows * (dv + 1) fp32).  num_parts <= 0 means
+ * ((batch + num_parts) slots of rows * (dv + 2) fp32).  num_parts <= 0 means
  * mla_default_num_parts of the current device.
  */
-int mla_workspace_size(int32_t batch, int32_t s_q, int32_t h_q, int32_t h_kv, int32_t dv,
+mla_status mla_workspace_size(int32_t batch, int32_t s_q, int32_t h_q, int32_t h_kv, int32_t dv,
                        int32_t num_parts, size_t* bytes);
 
 typedef struct mla_decode_params {
@@ -167,7 +171,7 @@ typedef struct mla_decode_params {
  * k_row_stride >= d; k_block_stride >= 63 * k_row_stride + d (a page's rows inside one
  * block stride); workspace 256-byte aligned.
  */
-int mla_decode_with_kvcache(const mla_decode_params* params, void* stream);
+mla_status mla_decode_with_kvcache(const mla_decode_params* params, void* stream);
 
 /* ---- Writes into the paged cache (the steps before a decode).
  *
@@ -195,11 +199,11 @@ int mla_decode_with_kvcache(const mla_decode_params* params, void* stream);
  * (a swap or re-layout).  A pair naming a page outside its pool is skipped.
  * Pairs must not write a page another pair of the same call reads or writes.
  */
-int mla_append_kv(const void* kv_c, int64_t kv_c_stride, const void* k_pe, int64_t k_pe_stride,
+mla_status mla_append_kv(const void* kv_c, int64_t kv_c_stride, const void* k_pe, int64_t k_pe_stride,
                   const int64_t* slot_mapping, int32_t num_tokens, void* k_cache, int32_t num_blocks,
                   int64_t k_block_stride, int64_t k_row_stride, void* stream);
 
-int mla_copy_blocks(const void* src_cache, int32_t src_num_blocks, int64_t src_block_stride,
+mla_status mla_copy_blocks(const void* src_cache, int32_t src_num_blocks, int64_t src_block_stride,
                     int64_t src_row_stride, void* dst_cache, int32_t dst_num_blocks, int64_t dst_block_stride,
                     int64_t dst_row_stride, const int64_t* block_mapping, int32_t num_pairs, void* stream);
 

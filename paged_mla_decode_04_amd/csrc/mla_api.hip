@@ -30,17 +30,18 @@ int cu_count(int device) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WorkspaceLayout {
-  size_t tile_md, num_splits, part_lse, part_o, total;
+  size_t tile_md, num_splits, part_lse, part_scale, part_o, total;
 };
 
-// [plan][partial lse][partial O]
+// [plan][partial lse][partial row scales][partial O]
 WorkspaceLayout layout(int64_t batch, int64_t rows, int64_t dv, int64_t num_parts) {
   WorkspaceLayout w;
   const int64_t slots = batch + num_parts;
   w.tile_md = 0;
   w.num_splits = align256((size_t)num_parts * mla::kTileMdInts * 4);
   w.part_lse = w.num_splits + align256((size_t)(batch + 1) * 4);
-  w.part_o = w.part_lse + align256((size_t)(slots * rows) * 4);
+  w.part_scale = w.part_lse + align256((size_t)(slots * rows) * 4);
+  w.part_o = w.part_scale + align256((size_t)(slots * rows) * 4);
   w.total = w.part_o + align256((size_t)(slots * rows * dv) * 4);
   return w;
 }
@@ -54,7 +55,7 @@ int default_parts(int device, int rows) {
   return per < 1 ? 1 : per;
 }
 
-int check_plan_args(int32_t batch, int32_t q_rows, int32_t h_kv, int32_t num_parts) {
+mla_status check_plan_args(int32_t batch, int32_t q_rows, int32_t h_kv, int32_t num_parts) {
   if (batch < 0 || q_rows <= 0 || h_kv <= 0 || num_parts <= 0) return MLA_ERR_BAD_SHAPE;
   if (q_rows % h_kv) return MLA_ERR_BAD_SHAPE;
   if (q_rows / h_kv > MLA_MAX_ROWS) return MLA_ERR_UNSUPPORTED;
@@ -66,7 +67,7 @@ int check_plan_args(int32_t batch, int32_t q_rows, int32_t h_kv, int32_t num_par
 
 extern "C" {
 
-const char* mla_status_string(int status) {
+const char* mla_status_string(mla_status status) {
   switch (status) {
     case MLA_OK: return "ok";
     case MLA_ERR_NULL_POINTER: return "a required pointer is NULL";
@@ -82,7 +83,7 @@ const char* mla_status_string(int status) {
 
 size_t mla_decode_params_size(void) { return sizeof(mla_decode_params); }
 
-int mla_default_num_parts(int device, int32_t q_rows, int32_t h_kv, int32_t* num_parts) {
+mla_status mla_default_num_parts(int device, int32_t q_rows, int32_t h_kv, int32_t* num_parts) {
   if (!num_parts) return MLA_ERR_NULL_POINTER;
   if (q_rows <= 0 || h_kv <= 0 || q_rows % h_kv) return MLA_ERR_BAD_SHAPE;
   const int p = default_parts(device, q_rows / h_kv);
@@ -91,10 +92,10 @@ int mla_default_num_parts(int device, int32_t q_rows, int32_t h_kv, int32_t* num
   return MLA_OK;
 }
 
-int mla_plan_host(const int32_t* cache_seqlens_h, int32_t batch, int32_t q_rows, int32_t h_kv,
+mla_status mla_plan_host(const int32_t* cache_seqlens_h, int32_t batch, int32_t q_rows, int32_t h_kv,
                   int32_t num_parts, int32_t* tile_md_h, int32_t* num_splits_h) {
   if ((!cache_seqlens_h && batch > 0) || !tile_md_h || !num_splits_h) return MLA_ERR_NULL_POINTER;
-  const int st = check_plan_args(batch, q_rows, h_kv, num_parts);
+  const mla_status st = check_plan_args(batch, q_rows, h_kv, num_parts);
   if (st != MLA_OK) return st;
   std::vector<int64_t> prefix((size_t)batch + 1);
   mla::plan_split_kv_host(cache_seqlens_h, batch, q_rows / h_kv, num_parts, tile_md_h, num_splits_h,
@@ -102,10 +103,10 @@ int mla_plan_host(const int32_t* cache_seqlens_h, int32_t batch, int32_t q_rows,
   return MLA_OK;
 }
 
-int mla_get_metadata(const int32_t* cache_seqlens_d, int32_t batch, int32_t q_rows, int32_t h_kv,
+mla_status mla_get_metadata(const int32_t* cache_seqlens_d, int32_t batch, int32_t q_rows, int32_t h_kv,
                      int32_t num_parts, int32_t* tile_md_d, int32_t* num_splits_d, void* stream) {
   if ((!cache_seqlens_d && batch > 0) || !tile_md_d || !num_splits_d) return MLA_ERR_NULL_POINTER;
-  const int st = check_plan_args(batch, q_rows, h_kv, num_parts);
+  const mla_status st = check_plan_args(batch, q_rows, h_kv, num_parts);
   if (st != MLA_OK) return st;
   if (batch > mla::kMaxPlanBatch) return MLA_ERR_UNSUPPORTED;
   if (mla::launch_plan(cache_seqlens_d, batch, q_rows / h_kv, num_parts, tile_md_d, num_splits_d,
@@ -114,7 +115,7 @@ int mla_get_metadata(const int32_t* cache_seqlens_d, int32_t batch, int32_t q_ro
   return MLA_OK;
 }
 
-int mla_workspace_size(int32_t batch, int32_t s_q, int32_t h_q, int32_t h_kv, int32_t dv,
+mla_status mla_workspace_size(int32_t batch, int32_t s_q, int32_t h_q, int32_t h_kv, int32_t dv,
                        int32_t num_parts, size_t* bytes) {
   if (!bytes) return MLA_ERR_NULL_POINTER;
   if (batch < 0 || s_q <= 0 || h_q <= 0 || h_kv <= 0 || dv <= 0 || h_q % h_kv) return MLA_ERR_BAD_SHAPE;
@@ -130,7 +131,7 @@ int mla_workspace_size(int32_t batch, int32_t s_q, int32_t h_q, int32_t h_kv, in
   return MLA_OK;
 }
 
-int mla_decode_with_kvcache(const mla_decode_params* p, void* stream) {
+mla_status mla_decode_with_kvcache(const mla_decode_params* p, void* stream) {
   if (!p) return MLA_ERR_NULL_POINTER;
   if (p->batch < 0 || p->s_q <= 0 || p->h_q <= 0 || p->h_kv <= 0 || p->num_blocks < 0 ||
       p->max_blocks_per_seq < 0 || p->block_size <= 0 || p->d <= 0 || p->dv <= 0)
@@ -212,6 +213,7 @@ int mla_decode_with_kvcache(const mla_decode_params* p, void* stream) {
   a.row_blocks = mla::row_blocks((int)rows);
   a.part_lse = (float*)(ws + w.part_lse);
   a.part_o = (float*)(ws + w.part_o);
+  a.part_scale = (float*)(ws + w.part_scale);
   a.out = (uint16_t*)p->out;
   a.o_sb = p->out_batch_stride;
   a.o_ss = p->out_seq_stride;

@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(const uint16_
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 // The layout rules a cache view must follow (elements; 16-byte pieces).
-int check_cache(const void* cache, int64_t num_blocks, int64_t block_stride, int64_t row_stride) {
+mla_status check_cache(const void* cache, int64_t num_blocks, int64_t block_stride, int64_t row_stride) {
   if (num_blocks < 0) return MLA_ERR_BAD_SHAPE;
   if (!aligned16(cache) || block_stride % 8 || row_stride % 8 || row_stride < 576) return MLA_ERR_BAD_STRIDE;
   if (block_stride < 63 * row_stride + 576) return MLA_ERR_BAD_STRIDE;
@@ -75,13 +75,13 @@ int check_cache(const void* cache, int64_t num_blocks, int64_t block_stride, int
 
 extern "C" {
 
-int mla_append_kv(const void* kv_c, int64_t kv_c_stride, const void* k_pe, int64_t k_pe_stride,
+mla_status mla_append_kv(const void* kv_c, int64_t kv_c_stride, const void* k_pe, int64_t k_pe_stride,
                   const int64_t* slot_mapping, int32_t num_tokens, void* k_cache, int32_t num_blocks,
                   int64_t k_block_stride, int64_t k_row_stride, void* stream) {
   if (num_tokens < 0) return MLA_ERR_BAD_SHAPE;
   if (num_tokens == 0) return MLA_OK;
   if (!kv_c || !k_pe || !slot_mapping || !k_cache) return MLA_ERR_NULL_POINTER;
-  const int st = check_cache(k_cache, num_blocks, k_block_stride, k_row_stride);
+  const mla_status st = check_cache(k_cache, num_blocks, k_block_stride, k_row_stride);
   if (st != MLA_OK) return st;
   if (!aligned16(kv_c) || !aligned16(k_pe) || kv_c_stride % 8 || k_pe_stride % 8 || kv_c_stride < 512 ||
       k_pe_stride < 64)
@@ -92,13 +92,13 @@ int mla_append_kv(const void* kv_c, int64_t kv_c_stride, const void* k_pe, int64
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
-int mla_copy_blocks(const void* src_cache, int32_t src_num_blocks, int64_t src_block_stride,
+mla_status mla_copy_blocks(const void* src_cache, int32_t src_num_blocks, int64_t src_block_stride,
                     int64_t src_row_stride, void* dst_cache, int32_t dst_num_blocks, int64_t dst_block_stride,
                     int64_t dst_row_stride, const int64_t* block_mapping, int32_t num_pairs, void* stream) {
   if (num_pairs < 0) return MLA_ERR_BAD_SHAPE;
   if (num_pairs == 0) return MLA_OK;
   if (!src_cache || !dst_cache || !block_mapping) return MLA_ERR_NULL_POINTER;
-  int st = check_cache(src_cache, src_num_blocks, src_block_stride, src_row_stride);
+  mla_status st = check_cache(src_cache, src_num_blocks, src_block_stride, src_row_stride);
   if (st != MLA_OK) return st;
   st = check_cache(dst_cache, dst_num_blocks, dst_block_stride, dst_row_stride);
   if (st != MLA_OK) return st;

@@ -57,7 +57,7 @@ constexpr int kSSteps = kD / 16;                  // 36 score k-steps
 constexpr int kColTiles = kDv / 32;               // 16 output column tiles
 constexpr int kCopiesW = 9;                       // 1 KB copies per wave per chunk
 constexpr int kKAhead = 4;                        // score K fragments in flight
-constexpr int kVAhead = 8;                        // value V^T fragments in flight
+constexpr int kVAhead = 7;                        // value V^T fragments in flight
 static_assert(kSmemW <= 160 * 1024, "LDS budget");
 static_assert(kThreadsW / 64 * kCopiesW * 1024 == kTileBytes, "copies cover the chunk");
 
@@ -297,6 +297,11 @@ __device__ __forceinline__ i32x4 desc_batch(const DecodeArgs& a, const PartInfo&
     const int n = __builtin_amdgcn_readlane(nk, k);
     int hi = chunk_count(n);
     if (sq == pi.seq_last && 2 * pi.page_end < hi) hi = 2 * pi.page_end;
+    // The plan counts pages of the stored length, the walk those of the
+    // length clamped to the block table: a planned segment that starts past
+    // the clamp still gets one (empty) chunk, so that its split slot is
+    // written and the next sequence's chunks are not skipped.
+    if (hi <= lo) hi = lo + 1;
     const int seg_lo = sq == pi.seq_begin ? 2 * pi.page_begin : 0;
     const int cnt = hi - lo;
     if (!found) {
@@ -635,16 +640,32 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
         if (hlf == 0) a.lse[(int64_t)D0.seq * a.l_sb + (int64_t)ri.qi * a.l_ss + (int64_t)ri.hh * a.l_sh] = lse;
       }
     } else if (pi.blk_row0 + 32 * w < a.rows) {
+      // fp16 partial (O / l) * 2^-e with 2^e the smallest power of two above
+      // the row's largest |O / l| (the row's two lanes agree on it), so that
+      // every element keeps 11 significant bits; 2^e goes to part_scale.
       // (rows past the last one store zeros into the tile's padding)
+      float mx = 0.f;
+      static_for<0, 4 * kColTiles>([&](auto ic) {
+        const f32x4 v = acc_read4<decltype(ic)::value>();
+        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+      });
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(mx), __float_as_int(mx), false, false);
+      mx = fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1])) * fabsf(inv);
+      // mx = f 2^e with f in [0.5, 1); an empty, NaN or overflowing row keeps e = 0
+      const int e = (mx > 0.f && mx < INFINITY) ? __builtin_amdgcn_frexp_expf(mx) : 0;
+      const float f = inv * __builtin_ldexpf(1.f, -e);
       uint8_t* pb = (uint8_t*)a.part_o + (int64_t)seg_slot * partial_slot_bytes(a.rows) +
                     (int64_t)((pi.blk_row0 >> 5) + w) * kPartialTileBytes + 16 * opaque(lane);
       static_for<0, 2 * kColTiles>([&](auto ic) {
         constexpr int I = decltype(ic)::value;  // tile I >> 1, elements 8 (I & 1) ..
-        const f32x4 v0 = acc_read4<2 * I>() * inv, v1 = acc_read4<2 * I + 1>() * inv;
-        *(bf16x8*)(pb + 1024 * I) = bf16x8{(__bf16)v0[0], (__bf16)v0[1], (__bf16)v0[2], (__bf16)v0[3],
-                                           (__bf16)v1[0], (__bf16)v1[1], (__bf16)v1[2], (__bf16)v1[3]};
+        const f32x4 v0 = acc_read4<2 * I>() * f, v1 = acc_read4<2 * I + 1>() * f;
+        *(f16x8*)(pb + 1024 * I) = f16x8{(_Float16)v0[0], (_Float16)v0[1], (_Float16)v0[2], (_Float16)v0[3],
+                                         (_Float16)v1[0], (_Float16)v1[1], (_Float16)v1[2], (_Float16)v1[3]};
       });
-      if (ri.ok && hlf == 0) a.part_lse[(int64_t)seg_slot * a.rows + row] = lse;
+      if (ri.ok && hlf == 0) {
+        a.part_lse[(int64_t)seg_slot * a.rows + row] = lse;
+        a.part_scale[(int64_t)seg_slot * a.rows + row] = __builtin_ldexpf(1.f, e);
+      }
     }
     acc_zero();
     asm volatile("s_nop 4" ::: "memory");

@@ -21,7 +21,8 @@ struct DecodeArgs {
   const int32_t* num_splits;
   int32_t num_parts, row_blocks;
   float* part_lse;             // [slots][rows]
-  float* part_o;               // narrow kernel: fp32 [slots][rows][512]; wide kernel: bf16 tiles (below)
+  float* part_o;               // narrow kernel: fp32 [slots][rows][512]; wide kernel: fp16 tiles (below)
+  float* part_scale;           // wide kernel: [slots][rows] power-of-two factor of each partial row
   uint16_t* out;               // bf16 bits
   int64_t o_sb, o_ss, o_sh;
   float* lse;
@@ -29,10 +30,13 @@ struct DecodeArgs {
 };
 
 // Wide kernel partials: per slot, ceil(rows / 32) tiles of 32 rows x 512
-// columns in bf16 (32 KB), stored in the accumulator layout: [tile][column
-// tile ct (16)][element pair gp (2)][lane (64)][8 bf16].  A lane (j = lane & 31,
+// columns in fp16 (32 KB), stored in the accumulator layout: [tile][column
+// tile ct (16)][element pair gp (2)][lane (64)][8 fp16].  A lane (j = lane & 31,
 // h = lane >> 5) holds row j, columns 32 ct + 8 g + 4 h + e for g = 2 gp,
-// 2 gp + 1 and e = 0..3.
+// 2 gp + 1 and e = 0..3.  Row r of slot s holds (O / l) * 2^-e_r with 2^e_r the
+// smallest power of two above the row's largest magnitude, so that every
+// element lies in (-1, 1) and keeps fp16's 11 significant bits;
+// part_scale[s][r] = 2^e_r undoes it.
 constexpr int kPartialTileBytes = 32 * 512 * 2;
 __host__ __device__ inline int64_t partial_slot_bytes(int rows) {
   return (int64_t)((rows + 31) / 32) * kPartialTileBytes;

@@ -613,7 +613,7 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   if (lane == 0) a.lse[(int64_t)b * a.l_sb + (int64_t)qi * a.l_ss + (int64_t)h * a.l_sh] = L;
 }
 
-// The same merge for the wide kernel's bf16 tile partials: one workgroup per
+// The same merge for the wide kernel's fp16 tile partials: one workgroup per
 // (sequence, 32-row tile); wave v merges column tiles 4 v .. 4 v + 3 of the
 // 32 rows in the accumulator layout the partials keep, then the tile goes
 // through LDS so that every output row is written as one 1 KB store.
@@ -657,13 +657,15 @@ __global__ __launch_bounds__(256) void combine_tiles_kernel(DecodeArgs a) {
   if (L != -INFINITY && !nan) {
     const uint8_t* src0 = (const uint8_t*)a.part_o + (int64_t)base * partial_slot_bytes(a.rows) +
                           (int64_t)rt * kPartialTileBytes + 8 * 1024 * v + 16 * lane;
+    const float* scale_p = a.part_scale + (int64_t)base * a.rows + row;
     for (int i = 0; i < ns; ++i) {
       const float x = ok ? lse_p[(int64_t)i * a.rows] : -INFINITY;
-      const float wgt = __builtin_amdgcn_exp2f((x - L) * kLog2e);
+      // the split's weight, times its row's power-of-two factor (an empty split weighs nothing)
+      const float wgt = x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((x - L) * kLog2e) * scale_p[(int64_t)i * a.rows];
       const uint8_t* src = src0 + (int64_t)i * partial_slot_bytes(a.rows);
 #pragma unroll
       for (int p = 0; p < 8; ++p) {
-        const bf16x8 pv = *(const bf16x8*)(src + 1024 * p);
+        const f16x8 pv = *(const f16x8*)(src + 1024 * p);
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[p][e] += wgt * (float)pv[e];
       }
@@ -790,25 +792,29 @@ __global__ __launch_bounds__(256) void combine_splits_kernel(DecodeArgs a) {
     if (ok && L != -INFINITY && L == L) {
       const uint8_t* src0 = (const uint8_t*)a.part_o + (int64_t)base * partial_slot_bytes(a.rows) +
                             (int64_t)rt * kPartialTileBytes + 2048 * ct + 16 * lane;
+      const float* scale_p = a.part_scale + (int64_t)base * a.rows + 32 * rt + j;
       for (int i0 = v; i0 < ns; i0 += 4 * kMergeUnroll) {
-        float x[kMergeUnroll];
-        bf16x8 d[kMergeUnroll][2];
+        float x[kMergeUnroll], sc[kMergeUnroll];
+        f16x8 d[kMergeUnroll][2];
 #pragma unroll
         for (int u = 0; u < kMergeUnroll; ++u) {
           const int i = i0 + 4 * u;
           if (i < ns) {
             x[u] = lse_p[(int64_t)i * a.rows + j];
+            sc[u] = scale_p[(int64_t)i * a.rows];
             const uint8_t* src = src0 + (int64_t)i * partial_slot_bytes(a.rows);
-            d[u][0] = *(const bf16x8*)src;
-            d[u][1] = *(const bf16x8*)(src + 1024);
+            d[u][0] = *(const f16x8*)src;
+            d[u][1] = *(const f16x8*)(src + 1024);
           } else {
             x[u] = -INFINITY;
-            d[u][0] = d[u][1] = bf16x8{};
+            sc[u] = 0.f;
+            d[u][0] = d[u][1] = f16x8{};
           }
         }
 #pragma unroll
         for (int u = 0; u < kMergeUnroll; ++u) {
-          const float wgt = __builtin_amdgcn_exp2f((x[u] - L) * kLog2e);
+          // the split's weight, times its row's power-of-two factor (an empty split weighs nothing)
+          const float wgt = x[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((x[u] - L) * kLog2e) * sc[u];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             acc[e] += wgt * (float)d[u][0][e];

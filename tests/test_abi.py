@@ -157,7 +157,8 @@ def test_workspace_size_formula(lib):
         assert lib.mla_workspace_size(b, s_q, h_q, 1, 512, parts, ctypes.byref(n)) == _lib.MLA_OK
         rows = s_q * h_q
         slots = b + parts
-        want = (a256(parts * 8 * 4) + a256((b + 1) * 4) + a256(slots * rows * 4)
+        # plan, partial lse, partial row scales, partial O
+        want = (a256(parts * 8 * 4) + a256((b + 1) * 4) + 2 * a256(slots * rows * 4)
                 + a256(slots * rows * 512 * 4))
         assert n.value == want
     assert lib.mla_workspace_size(2, 1, 16, 1, 512, 4, None) == _lib.MLA_ERR_NULL_POINTER
