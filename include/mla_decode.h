@@ -65,7 +65,9 @@ typedef enum mla_status {
   MLA_ERR_UNSUPPORTED = 4,          /* d != 576, dv != 512, block_size != 64, h_kv != 1, too many rows */
   MLA_ERR_WORKSPACE_TOO_SMALL = 5,  /* workspace_bytes < mla_workspace_size(...) */
   MLA_ERR_HIP = 6,                  /* the HIP runtime reported an error */
-  MLA_ERR_BAD_ARGUMENT = 7          /* any other invalid scalar (e.g. non-finite softmax_scale) */
+  MLA_ERR_BAD_ARGUMENT = 7,         /* any other invalid scalar (e.g. non-finite softmax_scale) */
+  MLA_ERR_SCRATCH_TOO_SMALL = 8     /* mla_decode_with_kvcache_noalloc: the call needs more than the
+                                       library's static scratch (MLA_NOALLOC_SCRATCH_BYTES) */
 } mla_status;
 
 /* int32 values per part in the tile-scheduler metadata. */
@@ -74,6 +76,8 @@ typedef enum mla_status {
 #define MLA_ROWS_PER_WORKGROUP 128
 /* Upper bound on s_q * h_q / h_kv. */
 #define MLA_MAX_ROWS 1024
+/* Bytes of static device scratch behind mla_decode_with_kvcache_noalloc, per GPU. */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 /* Static, NUL-terminated description of a status. */
 const char* mla_status_string(mla_status status);
@@ -172,6 +176,25 @@ typedef struct mla_decode_params {
  * block stride); workspace 256-byte aligned.
  */
 mla_status mla_decode_with_kvcache(const mla_decode_params* params, void* stream);
+
+/*
+ * The same decode for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The caller still passes every input and output in params; workspace and
+ * workspace_bytes are ignored.  The plan (when params->tile_md is NULL) and
+ * the per-split partial results go to a static device array inside the
+ * library instead: MLA_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, placed when
+ * the library's code is loaded on that GPU and held until the process ends.
+ * The call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine).  A call that needs more scratch than that returns
+ * MLA_ERR_SCRATCH_TOO_SMALL before anything is enqueued; b = 128 sequences of
+ * 128 query rows at the default part count of a 256-CU GPU need about 49 MB.
+ * Every call on one GPU uses that GPU's one array: calls whose executions
+ * overlap on one GPU (two streams, two threads) race and give undefined
+ * results, so serialise them.  Nothing needs clearing between calls: every
+ * scratch byte a call reads is written earlier by the same call.
+ */
+mla_status mla_decode_with_kvcache_noalloc(const mla_decode_params* params, void* stream);
 
 /* ---- Writes into the paged cache (the steps before a decode).
  *

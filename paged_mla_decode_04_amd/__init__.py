@@ -92,7 +92,7 @@ def mla_decode_with_kvcache(q: torch.Tensor, blocked_k: torch.Tensor, block_tabl
                             cache_seqlens: torch.Tensor, dv: int, softmax_scale: float,
                             causal: bool, *, metadata=None, num_parts: Optional[int] = None,
                             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                            workspace: Optional[torch.Tensor] = None):
+                            workspace: Optional[torch.Tensor] = None, no_alloc: bool = False):
     """Paged MLA decode.
 
     q           bf16 [b, s_q, h_q, 576], last dim contiguous
@@ -101,6 +101,8 @@ def mla_decode_with_kvcache(q: torch.Tensor, blocked_k: torch.Tensor, block_tabl
     block_table int32 [b, max_blocks_per_seq]
     cache_seqlens int32 [b]
     metadata    optional (tile_md, num_splits) from get_mla_metadata for these seqlens
+    no_alloc    use mla_decode_with_kvcache_noalloc: the library's static scratch
+                instead of a workspace (none is allocated; `workspace` is ignored)
     Returns (out bf16 [b, s_q, h_q, dv], lse fp32 [b, s_q, h_q]).
     """
     if q.dim() != 4 or blocked_k.dim() != 4 or block_table.dim() != 2:
@@ -131,9 +133,10 @@ def mla_decode_with_kvcache(q: torch.Tensor, blocked_k: torch.Tensor, block_tabl
         tile_md, num_splits = metadata
         num_parts = tile_md.shape[0]
     parts = 0 if num_parts is None else int(num_parts)
-    need = workspace_size(b, s_q, h_q, h_kv, dv, parts) if b else 256
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
+    if not no_alloc:
+        need = workspace_size(b, s_q, h_q, h_kv, dv, parts) if b else 256
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
     p = _lib.DecodeParams()
     p.q = q.data_ptr()
     p.q_batch_stride, p.q_seq_stride, p.q_head_stride = q.stride(0), q.stride(1), q.stride(2)
@@ -152,14 +155,14 @@ def mla_decode_with_kvcache(q: torch.Tensor, blocked_k: torch.Tensor, block_tabl
     p.tile_md = None if tile_md is None else tile_md.data_ptr()
     p.num_splits = None if num_splits is None else num_splits.data_ptr()
     p.num_parts = parts
-    p.workspace = workspace.data_ptr()
-    p.workspace_bytes = workspace.numel()
+    p.workspace = None if no_alloc else workspace.data_ptr()
+    p.workspace_bytes = 0 if no_alloc else workspace.numel()
     p.out = out.data_ptr()
     p.out_batch_stride, p.out_seq_stride, p.out_head_stride = out.stride(0), out.stride(1), out.stride(2)
     p.lse = lse.data_ptr()
     p.lse_batch_stride, p.lse_seq_stride, p.lse_head_stride = lse.stride(0), lse.stride(1), lse.stride(2)
-    _lib.check(_lib.load().mla_decode_with_kvcache(ctypes.byref(p), _stream(dev)),
-               "mla_decode_with_kvcache")
+    entry = "mla_decode_with_kvcache_noalloc" if no_alloc else "mla_decode_with_kvcache"
+    _lib.check(getattr(_lib.load(), entry)(ctypes.byref(p), _stream(dev)), entry)
     return out, lse
 
 

@@ -21,6 +21,8 @@ MLA_ERR_UNSUPPORTED = 4
 MLA_ERR_WORKSPACE_TOO_SMALL = 5
 MLA_ERR_HIP = 6
 MLA_ERR_BAD_ARGUMENT = 7
+MLA_ERR_SCRATCH_TOO_SMALL = 8
+NOALLOC_SCRATCH_BYTES = 64 << 20
 TILE_MD_INTS = 8
 ROWS_PER_WORKGROUP = 128
 MAX_ROWS = 1024
@@ -33,6 +35,7 @@ EXPORTS = (
     "mla_plan_host",
     "mla_workspace_size",
     "mla_decode_with_kvcache",
+    "mla_decode_with_kvcache_noalloc",
     "mla_append_kv",
     "mla_copy_blocks",
 )
@@ -97,6 +100,8 @@ def load():
                                            ctypes.POINTER(ctypes.c_size_t)]
         lib.mla_decode_with_kvcache.restype = ctypes.c_int
         lib.mla_decode_with_kvcache.argtypes = [ctypes.POINTER(DecodeParams), c_p]
+        lib.mla_decode_with_kvcache_noalloc.restype = ctypes.c_int
+        lib.mla_decode_with_kvcache_noalloc.argtypes = [ctypes.POINTER(DecodeParams), c_p]
         lib.mla_append_kv.restype = ctypes.c_int
         lib.mla_append_kv.argtypes = [c_p, c_i64, c_p, c_i64, c_p, c_i32, c_p, c_i32, c_i64, c_i64, c_p]
         lib.mla_copy_blocks.restype = ctypes.c_int
@@ -117,6 +122,7 @@ def status_string(status: int) -> str:
 def check(status: int, what: str) -> None:
     if status != MLA_OK:
         if status in (MLA_ERR_BAD_SHAPE, MLA_ERR_BAD_STRIDE, MLA_ERR_UNSUPPORTED,
-                      MLA_ERR_WORKSPACE_TOO_SMALL, MLA_ERR_NULL_POINTER, MLA_ERR_BAD_ARGUMENT):
+                      MLA_ERR_WORKSPACE_TOO_SMALL, MLA_ERR_NULL_POINTER, MLA_ERR_BAD_ARGUMENT,
+                      MLA_ERR_SCRATCH_TOO_SMALL):
             raise ValueError(f"{what}: {status_string(status)} (status {status})")
         raise MLAError(status, what)
