@@ -6,8 +6,9 @@ CPU-baseline leg may import anything from this package.  The product path
 its native library is missing instead of falling back to this code.
 
 Modules:
-  mla_ref -- the fp64 NumPy definition (mla_decode_ref) and the lse merge of
-             key-range partials (merge_partials).
+  mla_ref -- the fp64 NumPy definition (mla_decode_ref, over a bf16 or an
+             FP8 E4M3 cache) and the lse merge of key-range partials
+             (merge_partials).
   brute   -- a scalar pure-Python statement of the same definition, used to
              pin mla_ref on tiny inputs.
 
@@ -17,8 +18,8 @@ print no out/lse values, so agreement with any published implementation is
 not pinned.
 """
 
-from .mla_ref import (bf16_bits_to_f64, visible_keys, gather_tokens, softmax_average,
-                      attend_rows, mla_decode_ref, merge_partials)
+from .mla_ref import (bf16_bits_to_f64, e4m3_bits_to_f64, visible_keys, gather_tokens,
+                      softmax_average, attend_rows, mla_decode_ref, merge_partials)
 
-__all__ = ["bf16_bits_to_f64", "visible_keys", "gather_tokens", "softmax_average",
-           "attend_rows", "mla_decode_ref", "merge_partials"]
+__all__ = ["bf16_bits_to_f64", "e4m3_bits_to_f64", "visible_keys", "gather_tokens",
+           "softmax_average", "attend_rows", "mla_decode_ref", "merge_partials"]

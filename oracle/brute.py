@@ -27,10 +27,33 @@ def bf16_to_float(bits: int) -> float:
     return struct.unpack("<f", struct.pack("<I", (int(bits) & 0xFFFF) << 16))[0]
 
 
+def e4m3_to_float(byte: int) -> float:
+    """An FP8 E4M3 byte (OCP "fn" variant) from its fields, written as an
+    integer significand times a power of two: 8 + m for a normal number
+    (exponent field e > 0), m for a subnormal, scaled by 2^(max(e, 1) - 10);
+    the code with every exponent and mantissa bit set is NaN."""
+    byte = int(byte) & 0xFF
+    e, m = (byte >> 3) & 0xF, byte & 0x7
+    if e == 0xF and m == 0x7:
+        return math.nan
+    sig = (8 + m) if e > 0 else m
+    val = math.ldexp(sig, max(e, 1) - 10)
+    return -val if byte & 0x80 else val
+
+
 def brute_decode(q_bits, k_bits, block_table, cache_seqlens, softmax_scale, causal,
-                 d=576, dv=512, block_size=64):
+                 d=576, dv=512, block_size=64, kv_format="bf16", kv_scale=1.0):
     """q_bits[b][i][h][c], k_bits[page][row][g][c]: nested sequences (or arrays)
-    of raw bf16 bits.  Returns nested lists out[b][i][h][c] and lse[b][i][h]."""
+    of raw bf16 bits, or for kv_format "fp8_e4m3" raw E4M3 cache bytes whose
+    values are times kv_scale.  Returns nested lists out[b][i][h][c] and
+    lse[b][i][h]."""
+    if kv_format == "bf16":
+        kdec = bf16_to_float
+    elif kv_format == "fp8_e4m3":
+        def kdec(x):
+            return e4m3_to_float(x) * kv_scale
+    else:
+        raise ValueError(kv_format)
     B = len(q_bits)
     out, lse = [], []
     for b in range(B):
@@ -52,7 +75,7 @@ def brute_decode(q_bits, k_bits, block_table, cache_seqlens, softmax_scale, caus
                 for t in range(max(visible, 0)):
                     page = int(block_table[b][t // block_size])
                     row = t % block_size
-                    kt = [bf16_to_float(k_bits[page][row][g][c]) for c in range(d)]
+                    kt = [kdec(k_bits[page][row][g][c]) for c in range(d)]
                     scores.append(softmax_scale * math.fsum(qs[c] * kt[c] for c in range(d)))
                     vrows.append(kt[:dv])
                 if not scores:

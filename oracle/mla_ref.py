@@ -59,6 +59,26 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return u.view(np.float32).astype(np.float64)
 
 
+def e4m3_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Decode raw FP8 E4M3 bytes (the OCP "fn" variant) exactly into float64.
+
+    One sign bit, four exponent bits with bias 7, three mantissa bits, no
+    infinities:
+      exponent 0:        (-1)^s * 2^-6 * m / 8          (zero and subnormals)
+      exponent 1..15:    (-1)^s * 2^(e - 7) * (1 + m / 8)
+      exponent 15, m 7:  NaN (the format's only non-finite code, 0x7F / 0xFF)
+    The largest finite magnitude is 448 (0x7E), the smallest 2^-9 (0x01).
+    Reading of the FP8 latent cache (see fp8 cache in mla_decode_ref).
+    """
+    b = np.asarray(bits).astype(np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 0x7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+    val = sign * mag
+    return np.where((e == 15) & (b & 0x7 == 7), np.nan, val)
+
+
 def visible_keys(n: int, s_q: int, i: int, causal: bool) -> int:
     """How many leading keys query token i of s_q sees in an n-token cache.
 
@@ -72,18 +92,26 @@ def visible_keys(n: int, s_q: int, i: int, causal: bool) -> int:
 
 
 def gather_tokens(k_bits: np.ndarray, table_row: np.ndarray, n: int, kv_head: int,
-                  block_size: int = BLOCK_SIZE, d: int = D_QK) -> np.ndarray:
+                  block_size: int = BLOCK_SIZE, d: int = D_QK, kv_format: str = "bf16",
+                  kv_scale: float = 1.0) -> np.ndarray:
     """Logical tokens 0..n-1 of one sequence as an (n, d) fp64 matrix.
 
     Token t lives in physical page table_row[t // block_size], row
     t % block_size ([PAI] section 二.4: the cache is blocked by pages that the
     block table maps).  Only the first d elements of each entry are read
-    ([PR12676]: the padded tail is never viewed).
+    ([PR12676]: the padded tail is never viewed).  An fp8 cache
+    (kv_format "fp8_e4m3") holds one E4M3 byte per element; its value is the
+    decoded byte times the cache's scale kv_scale.
     """
     t = np.arange(n)
     phys = np.asarray(table_row)[t // block_size].astype(np.int64)
     rows = t % block_size
-    return bf16_bits_to_f64(k_bits[phys, rows, kv_head, :d])
+    raw = k_bits[phys, rows, kv_head, :d]
+    if kv_format == "bf16":
+        return bf16_bits_to_f64(raw)
+    if kv_format == "fp8_e4m3":
+        return e4m3_bits_to_f64(raw) * float(kv_scale)
+    raise ValueError(f"unknown cache format {kv_format!r}")
 
 
 def softmax_average(scores: np.ndarray, values: np.ndarray):
@@ -122,16 +150,24 @@ def attend_rows(q_rows: np.ndarray, K: np.ndarray, counts, softmax_scale: float,
 def mla_decode_ref(q_bits: np.ndarray, k_bits: np.ndarray, block_table: np.ndarray,
                    cache_seqlens: np.ndarray, softmax_scale: float, causal: bool,
                    dv: int = D_V, batch_indices=None, block_size: int = BLOCK_SIZE,
-                   token_range=None):
+                   token_range=None, kv_format: str = "bf16", kv_scale: float = 1.0):
     """The oracle.
 
     q_bits:   uint16 [b, s_q, h_q, d]       raw bf16 bits of the queries
-    k_bits:   uint16 [num_blocks, block_size, h_kv, pitch >= d]  raw bf16 cache bits
+    k_bits:   [num_blocks, block_size, h_kv, pitch >= d] raw cache elements:
+              uint16 bf16 bits, or (kv_format "fp8_e4m3") uint8 E4M3 bytes
+              whose values are scaled by kv_scale
     block_table: int [b, max_blocks_per_seq]
     cache_seqlens: int [b]
     batch_indices: optional subset of sequences to compute (others stay 0 / -inf)
     token_range: optional (begin, end) to restrict every row to keys in
                  [begin, end) -- the partial result of one key split.
+
+    The fp8 cache is our reading of the FP8 latent cache the Hacker News
+    discussion of the FlashMLA release links to (vLLM's MLA and FP8 work):
+    the whole 576-element entry stored as E4M3 bytes with one scale per
+    cache; K and V are the dequantised values, so the definition above is
+    unchanged.
 
     Returns fp64 out [b, s_q, h_q, dv] and lse [b, s_q, h_q].
     """
@@ -146,7 +182,7 @@ def mla_decode_ref(q_bits: np.ndarray, k_bits: np.ndarray, block_table: np.ndarr
     for bi in todo:
         n = int(cache_seqlens[bi])
         for g in range(h_kv):
-            K = gather_tokens(k_bits, block_table[bi], n, g, block_size, d)
+            K = gather_tokens(k_bits, block_table[bi], n, g, block_size, d, kv_format, kv_scale)
             heads = np.arange(g * group, (g + 1) * group)
             q_rows = bf16_bits_to_f64(q_bits[bi][:, heads, :]).reshape(s_q * group, d)
             counts = np.repeat([visible_keys(n, s_q, i, causal) for i in range(s_q)], group)

@@ -31,6 +31,8 @@ BLOCK_SIZE = 64     # tokens per page
 DEFAULT_SCALE = 1.0 / math.sqrt(192.0)
 
 BF16_QUIET_NAN_BITS = 0x7FC0
+E4M3_NAN_BYTE = 0x7F
+FP8_KV_SCALE = 1.0 / 64.0    # a power of two: N(0,1) values / scale stay inside +-448
 
 
 @dataclass(frozen=True)
@@ -49,6 +51,8 @@ class Workload:
     softmax_scale: float = DEFAULT_SCALE
     fixed_seqlens: Optional[tuple] = None
     description: str = ""
+    kv_format: str = "bf16"      # "bf16" | "fp8_e4m3" (one E4M3 byte per element)
+    kv_scale: float = 1.0        # value of an fp8 element = decoded byte * kv_scale
 
 
 # The five workloads: a tiny one, a DeepSeek-V2-Lite-shaped one (16 heads),
@@ -100,6 +104,14 @@ class DecodeInputs:
     def causal(self) -> bool:
         return self.workload.causal
 
+    @property
+    def kv_format(self) -> str:
+        return self.workload.kv_format
+
+    @property
+    def kv_scale(self) -> float:
+        return self.workload.kv_scale
+
     def to(self, device) -> "DecodeInputs":
         """Copy to a device, keeping the cache's pitch (the padded storage moves whole)."""
         storage = self.k_storage.to(device)
@@ -143,7 +155,8 @@ def draw(w: Workload | str, seed: int = 0, *, seqlens_override=None,
     seqlens_override replaces the recipe (same draw order afterwards).
     poison=True fills every cache byte the result must not depend on (pad
     columns, rows past each sequence's length, pages no sequence uses) with
-    bf16 NaN, and the block-table entries past each sequence's last page with
+    NaN (bf16 NaN bits, or the E4M3 NaN byte 0x7F of an fp8 cache), and the
+    block-table entries past each sequence's last page with
     -1.
     """
     if isinstance(w, str):
@@ -163,7 +176,14 @@ def draw(w: Workload | str, seed: int = 0, *, seqlens_override=None,
 
     q = torch.randn(b, w.s_q, w.h_q, D_QK, generator=gen, dtype=torch.float32).to(torch.bfloat16)
     k_storage = torch.randn(num_blocks, BLOCK_SIZE, w.h_kv, w.pitch, generator=gen,
-                            dtype=torch.float32).to(torch.bfloat16)
+                            dtype=torch.float32)
+    if w.kv_format == "fp8_e4m3":
+        # the same N(0,1) values stored as E4M3 bytes of x / kv_scale (torch's
+        # round-to-nearest conversion, inside the format's +-448)
+        k_storage = (k_storage / w.kv_scale).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+        k_storage = k_storage.view(torch.uint8)
+    else:
+        k_storage = k_storage.to(torch.bfloat16)
     if w.table == "arange":
         table = torch.arange(num_blocks, dtype=torch.int32).view(b, width)
     else:
@@ -178,8 +198,12 @@ def draw(w: Workload | str, seed: int = 0, *, seqlens_override=None,
 
 
 def _poison(k_storage: torch.Tensor, table: torch.Tensor, seqlens: torch.Tensor) -> None:
-    bits = k_storage.view(torch.int16)
-    nan = torch.tensor(BF16_QUIET_NAN_BITS, dtype=torch.int16)
+    if k_storage.dtype == torch.uint8:  # fp8 cache: 0x7F is E4M3's NaN
+        bits = k_storage
+        nan = torch.tensor(E4M3_NAN_BYTE, dtype=torch.uint8)
+    else:
+        bits = k_storage.view(torch.int16)
+        nan = torch.tensor(BF16_QUIET_NAN_BITS, dtype=torch.int16)
     if k_storage.shape[-1] > D_QK:
         bits[..., D_QK:] = nan
     used = torch.zeros(k_storage.shape[0], dtype=torch.bool)
