@@ -166,14 +166,29 @@ typedef struct mla_decode_params {
   int64_t out_batch_stride, out_seq_stride, out_head_stride;
   float* lse;
   int64_t lse_batch_stride, lse_seq_stride, lse_head_stride;
+
+  /* cache element type (0 in a zero-initialised struct: bf16).  MLA_KV_FP8_E4M3: every
+     element is one OCP FP8 E4M3 byte whose value is its decode times kv_scale (one scale per
+     cache, finite and > 0; ignored for bf16).  k_*_stride count elements of this type. */
+  int32_t kv_dtype;
+  float kv_scale;
 } mla_decode_params;
+
+/* mla_decode_params.kv_dtype values */
+#define MLA_KV_BF16 0
+#define MLA_KV_FP8_E4M3 1
 
 /*
  * Enqueue the decode (plan if needed, split-KV attention, lse merge) on `stream` and
  * return.  Alignment rules (MLA_ERR_BAD_STRIDE otherwise): q, k_cache and out 16-byte
- * aligned; q_*_stride, k_*_stride and out_*_stride multiples of 8 elements;
- * k_row_stride >= d; k_block_stride >= 63 * k_row_stride + d (a page's rows inside one
- * block stride); workspace 256-byte aligned.
+ * aligned; q_*_stride and out_*_stride multiples of 8 elements; k_*_stride multiples of
+ * 16 bytes (8 bf16 or 16 fp8 elements); k_row_stride >= d; k_block_stride >= 63 *
+ * k_row_stride + d (a page's rows inside one block stride); workspace 256-byte aligned.
+ *
+ * An fp8 cache (kv_dtype MLA_KV_FP8_E4M3) is our reading of the FP8 latent cache the
+ * Hacker News discussion of the FlashMLA release links to (vLLM's MLA and FP8 work): K is
+ * the 576 decoded elements times kv_scale and V their first 512, exactly as for bf16; the
+ * queries and out stay bf16.  It runs on the 128-row kernel whatever the row count.
  */
 mla_status mla_decode_with_kvcache(const mla_decode_params* params, void* stream);
 

@@ -92,12 +92,15 @@ def mla_decode_with_kvcache(q: torch.Tensor, blocked_k: torch.Tensor, block_tabl
                             cache_seqlens: torch.Tensor, dv: int, softmax_scale: float,
                             causal: bool, *, metadata=None, num_parts: Optional[int] = None,
                             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                            workspace: Optional[torch.Tensor] = None, no_alloc: bool = False):
+                            workspace: Optional[torch.Tensor] = None, no_alloc: bool = False,
+                            kv_scale: Optional[float] = None):
     """Paged MLA decode.
 
     q           bf16 [b, s_q, h_q, 576], last dim contiguous
     blocked_k   bf16 [num_blocks, 64, h_kv, 576] (any strided view with unit last-dim
-                stride, e.g. the first 576 elements of a [num_blocks, 64, h_kv, 640] cache)
+                stride, e.g. the first 576 elements of a [num_blocks, 64, h_kv, 640] cache),
+                or an fp8 cache of the same shape: uint8 or float8_e4m3fn E4M3 bytes whose
+                values are times kv_scale (required then)
     block_table int32 [b, max_blocks_per_seq]
     cache_seqlens int32 [b]
     metadata    optional (tile_md, num_splits) from get_mla_metadata for these seqlens
@@ -107,8 +110,11 @@ def mla_decode_with_kvcache(q: torch.Tensor, blocked_k: torch.Tensor, block_tabl
     """
     if q.dim() != 4 or blocked_k.dim() != 4 or block_table.dim() != 2:
         raise ValueError("q and blocked_k must be 4-D, block_table 2-D")
-    if q.dtype != torch.bfloat16 or blocked_k.dtype != torch.bfloat16:
-        raise ValueError("q and blocked_k must be bfloat16")
+    fp8 = blocked_k.dtype in (torch.uint8, torch.float8_e4m3fn)
+    if q.dtype != torch.bfloat16 or not (fp8 or blocked_k.dtype == torch.bfloat16):
+        raise ValueError("q must be bfloat16 and blocked_k bfloat16 or E4M3 bytes")
+    if fp8 and kv_scale is None:
+        raise ValueError("an fp8 cache needs its kv_scale")
     if block_table.dtype != torch.int32 or cache_seqlens.dtype != torch.int32:
         raise ValueError("block_table and cache_seqlens must be int32")
     dev = q.device
@@ -161,6 +167,8 @@ def mla_decode_with_kvcache(q: torch.Tensor, blocked_k: torch.Tensor, block_tabl
     p.out_batch_stride, p.out_seq_stride, p.out_head_stride = out.stride(0), out.stride(1), out.stride(2)
     p.lse = lse.data_ptr()
     p.lse_batch_stride, p.lse_seq_stride, p.lse_head_stride = lse.stride(0), lse.stride(1), lse.stride(2)
+    p.kv_dtype = _lib.KV_FP8_E4M3 if fp8 else _lib.KV_BF16
+    p.kv_scale = float(kv_scale) if fp8 else 1.0
     entry = "mla_decode_with_kvcache_noalloc" if no_alloc else "mla_decode_with_kvcache"
     _lib.check(getattr(_lib.load(), entry)(ctypes.byref(p), _stream(dev)), entry)
     return out, lse

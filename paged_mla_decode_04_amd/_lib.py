@@ -24,6 +24,8 @@ MLA_ERR_BAD_ARGUMENT = 7
 MLA_ERR_SCRATCH_TOO_SMALL = 8
 NOALLOC_SCRATCH_BYTES = 64 << 20
 TILE_MD_INTS = 8
+KV_BF16 = 0
+KV_FP8_E4M3 = 1
 ROWS_PER_WORKGROUP = 128
 MAX_ROWS = 1024
 
@@ -59,6 +61,7 @@ class DecodeParams(ctypes.Structure):
         ("workspace", c_p), ("workspace_bytes", ctypes.c_size_t),
         ("out", c_p), ("out_batch_stride", c_i64), ("out_seq_stride", c_i64), ("out_head_stride", c_i64),
         ("lse", c_p), ("lse_batch_stride", c_i64), ("lse_seq_stride", c_i64), ("lse_head_stride", c_i64),
+        ("kv_dtype", c_i32), ("kv_scale", ctypes.c_float),
     ]
 
 

@@ -38,7 +38,8 @@ struct WorkspaceLayout {
 // is sized for fp32 partial rows whichever kernel runs; `compact` sizes the
 // partial O for the kernel that runs instead (the wide kernel keeps fp16
 // tiles), which is what the static scratch of the no-allocation call holds.
-WorkspaceLayout layout(int64_t batch, int64_t rows, int64_t dv, int64_t num_parts, bool compact = false) {
+WorkspaceLayout layout(int64_t batch, int64_t rows, int64_t dv, int64_t num_parts, bool compact = false,
+                       bool wide = false) {
   WorkspaceLayout w;
   const int64_t slots = batch + num_parts;
   w.tile_md = 0;
@@ -46,7 +47,6 @@ WorkspaceLayout layout(int64_t batch, int64_t rows, int64_t dv, int64_t num_part
   w.part_lse = w.num_splits + align256((size_t)(batch + 1) * 4);
   w.part_scale = w.part_lse + align256((size_t)(slots * rows) * 4);
   w.part_o = w.part_scale + align256((size_t)(slots * rows) * 4);
-  const bool wide = mla::rows_per_block((int)rows) == mla::kRowsPerWorkgroup;
   const size_t o_bytes = compact && wide ? (size_t)slots * (size_t)mla::partial_slot_bytes(rows)
                                          : (size_t)(slots * rows * dv) * 4;
   w.total = w.part_o + align256(o_bytes);
@@ -109,6 +109,10 @@ mla_status decode_call(const mla_decode_params* p, void* stream, bool no_alloc) 
   const int64_t rows = (int64_t)p->s_q * p->h_q / p->h_kv;
   if (rows > MLA_MAX_ROWS) return MLA_ERR_UNSUPPORTED;
   if (!(p->softmax_scale == p->softmax_scale) || isinf(p->softmax_scale)) return MLA_ERR_BAD_ARGUMENT;
+  if (p->kv_dtype != MLA_KV_BF16 && p->kv_dtype != MLA_KV_FP8_E4M3) return MLA_ERR_BAD_ARGUMENT;
+  const bool kv8 = p->kv_dtype == MLA_KV_FP8_E4M3;
+  if (kv8 && !(p->kv_scale > 0.f && isfinite(p->kv_scale))) return MLA_ERR_BAD_ARGUMENT;
+  const int64_t kelem = kv8 ? 1 : 2;  // bytes per cache element
   if (p->batch == 0) return MLA_OK;
   if (!p->q || !p->k_cache || !p->block_table || !p->cache_seqlens || !p->out || !p->lse ||
       (!no_alloc && !p->workspace))
@@ -119,7 +123,8 @@ mla_status decode_call(const mla_decode_params* p, void* stream, bool no_alloc) 
   if (!no_alloc && ((uintptr_t)p->workspace & 255) != 0) return MLA_ERR_BAD_STRIDE;
   if (p->q_batch_stride % 8 || p->q_seq_stride % 8 || p->q_head_stride % 8) return MLA_ERR_BAD_STRIDE;
   if (p->out_batch_stride % 8 || p->out_seq_stride % 8 || p->out_head_stride % 8) return MLA_ERR_BAD_STRIDE;
-  if (p->k_block_stride % 8 || p->k_row_stride % 8 || p->k_row_stride < p->d) return MLA_ERR_BAD_STRIDE;
+  if ((p->k_block_stride * kelem) % 16 || (p->k_row_stride * kelem) % 16 || p->k_row_stride < p->d)
+    return MLA_ERR_BAD_STRIDE;
   if (p->k_block_stride < 0 || p->q_batch_stride < 0 || p->q_seq_stride < 0 || p->q_head_stride < 0 ||
       p->out_batch_stride < 0 || p->out_seq_stride < 0 || p->out_head_stride < 0 ||
       p->lse_batch_stride < 0 || p->lse_seq_stride < 0 || p->lse_head_stride < 0)
@@ -127,7 +132,7 @@ mla_status decode_call(const mla_decode_params* p, void* stream, bool no_alloc) 
   if (p->block_table_stride < p->max_blocks_per_seq) return MLA_ERR_BAD_STRIDE;
   // a page's 64 rows lie inside one block stride (the copy reads rows 0..63 of a block)
   if (p->k_block_stride < (int64_t)(p->block_size - 1) * p->k_row_stride + p->d) return MLA_ERR_BAD_STRIDE;
-  if ((int64_t)64 * p->k_row_stride * 2 > INT32_MAX) return MLA_ERR_BAD_STRIDE;
+  if ((int64_t)64 * p->k_row_stride * kelem > INT32_MAX) return MLA_ERR_BAD_STRIDE;
   if ((int64_t)p->max_blocks_per_seq * 64 > INT32_MAX) return MLA_ERR_BAD_SHAPE;
 
   int num_parts = p->num_parts;
@@ -140,7 +145,8 @@ mla_status decode_call(const mla_decode_params* p, void* stream, bool no_alloc) 
     if (num_parts < 0) return MLA_ERR_HIP;
   }
   if (num_parts > (1 << 20)) return MLA_ERR_BAD_SHAPE;
-  const WorkspaceLayout w = layout(p->batch, rows, p->dv, num_parts, no_alloc);
+  const bool wide = kv8 || mla::rows_per_block((int)rows) == mla::kRowsPerWorkgroup;
+  const WorkspaceLayout w = layout(p->batch, rows, p->dv, num_parts, no_alloc, wide);
   uint8_t* ws = (uint8_t*)p->workspace;
   if (no_alloc) {
     if (w.total > kScratchBytes) return MLA_ERR_SCRATCH_TOO_SMALL;
@@ -171,8 +177,8 @@ mla_status decode_call(const mla_decode_params* p, void* stream, bool no_alloc) 
   a.q_ss = p->q_seq_stride;
   a.q_sh = p->q_head_stride;
   a.k = (const uint8_t*)p->k_cache;
-  a.k_block_bytes = p->k_block_stride * 2;
-  a.k_row_bytes = p->k_row_stride * 2;
+  a.k_block_bytes = p->k_block_stride * kelem;
+  a.k_row_bytes = p->k_row_stride * kelem;
   a.num_blocks = p->num_blocks;
   a.block_table = p->block_table;
   a.bt_stride = p->block_table_stride;
@@ -183,7 +189,10 @@ mla_status decode_call(const mla_decode_params* p, void* stream, bool no_alloc) 
   a.h_q = p->h_q;
   a.rows = (int32_t)rows;
   a.causal = p->causal ? 1 : 0;
-  a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  a.scale_log2 = kv8 ? (float)((double)p->softmax_scale * (double)p->kv_scale * 1.4426950408889634)
+                    : p->softmax_scale * 1.4426950408889634f;
+  a.kv8 = kv8 ? 1 : 0;
+  a.kv_scale = kv8 ? p->kv_scale : 1.f;
   a.tile_md = tile_md;
   a.num_splits = num_splits;
   a.num_parts = num_parts;

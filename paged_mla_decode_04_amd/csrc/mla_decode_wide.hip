@@ -60,20 +60,34 @@ constexpr int kKAhead = 4;                        // score K fragments in flight
 constexpr int kVAhead = 7;                        // value V^T fragments in flight
 static_assert(kSmemW <= 160 * 1024, "LDS budget");
 static_assert(kThreadsW / 64 * kCopiesW * 1024 == kTileBytes, "copies cover the chunk");
+// An fp8 cache (one E4M3 byte per element): a wave's token octet of a chunk
+// (8 x 576 bytes) is staged as five 1 KB copies, then converted to bf16 into
+// one of three chunk slots the score and value products read as before.
+constexpr int kCopies8 = 5;
+constexpr int kStageWave = kCopies8 * 1024;       // 5120
+constexpr int kStageBytes = 4 * kStageWave;       // 20480
+constexpr int kSlots8 = 3;
+constexpr int kSmem8 = kSlots8 * kTileBytes + 2 * kStageBytes;  // 151552
+static_assert(kSmem8 <= 160 * 1024, "LDS budget (fp8 cache)");
+static_assert(8 * 576 <= kStageWave, "staging covers a token octet");
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 // Swizzle of token a's eight 16-byte chunks in a column block (uses bits 1..3
 // of a, so it repeats every 16 tokens).
 __device__ __forceinline__ int swz(int a) { return (((a >> 1) & 1) << 2) | ((a >> 2) & 3); }
 
-// Column block Q (1 KB) of the wave's token octet: source at lane_off + 128 Q
-// (the immediate offset), LDS at wave_base + 4096 Q (the immediate offset is
-// added to the LDS address too, so M0 is lowered by it).
-template <int Q>
+// Copy Q (1 KB) of the wave's token octet: source at lane_off + 128 Q (the
+// immediate offset), LDS at wave_base + LSTRIDE Q (the immediate offset is
+// added to the LDS address too, so M0 is lowered by it).  A bf16 cache copies
+// column block Q (LSTRIDE 4096, the block's place in a chunk slot), an fp8
+// cache byte range 128 Q .. 128 Q + 127 of each row (LSTRIDE 1024, staging).
+template <int Q, uint32_t LSTRIDE = 4096u>
 __device__ __forceinline__ void copy_block(__amdgpu_buffer_rsrc_t rsrc, uint32_t lane_off, uint32_t wave_base) {
   asm volatile("buffer_load_dwordx4 %0, %1, 0 offen offset:%2 lds" ::"v"(lane_off), "s"(rsrc), "n"(128 * Q),
-               "{m0}"(wave_base + (4096u - 128u) * Q)
+               "{m0}"(wave_base + (LSTRIDE - 128u) * Q)
                : "memory");
 }
 
@@ -364,8 +378,10 @@ __device__ __forceinline__ Chunk batch_get(const i32x4& b, int i) {
 }
 
 
+template <bool KV8>
 __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmemW];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[KV8 ? kSmem8 : kSmemW];
+  constexpr int kCopies = KV8 ? kCopies8 : kCopiesW;
   const int w = uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   PartInfo pi;
@@ -422,20 +438,59 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
   // and read nothing, and every step issues the same nine loads.  Column block
   // q is the load's immediate offset 128 q, which an LDS-direct load also adds
   // to its LDS address, so M0 is lowered by as much.
+  // An fp8 cache's copy Q moves 16-byte pieces 8 Q .. 8 Q + 7 of the octet's
+  // rows: lane l takes token 8 w + (l >> 3), piece 8 Q + (l & 7), so that the
+  // wave's staging holds piece c of its token a at 1024 (c / 8) + 128 a +
+  // 16 (c % 8).  Pieces 36..39 (copy 4, lanes with l & 7 >= 4) lie past the
+  // 576 bytes of the entry: they land in staging and are never converted.
   const uint32_t cp_lane = [&] {
     const int tk = 8 * w + (lane >> 3);
+    if constexpr (KV8) return (uint32_t)tk * row_bytes + 16u * (uint32_t)(lane & 7);
     return (uint32_t)tk * row_bytes + 16u * (uint32_t)((lane & 7) ^ swz(tk));
   }();
   auto copy_rsrc = [&](const Chunk& c) -> __amdgpu_buffer_rsrc_t {
     const Chunk cz = c.valid() ? c : Chunk{0, 0, 0, 0, false, false, true};
     return chunk_rsrc(a, cz);
   };
+  // (slot_addr: the chunk slot for a bf16 cache, the staging slot for fp8)
   auto copy_one = [&](__amdgpu_buffer_rsrc_t rsrc, uint32_t slot_addr, auto qc) {
-    copy_block<decltype(qc)::value>(rsrc, cp_lane, slot_addr + 1024u * w);
+    if constexpr (KV8)
+      copy_block<decltype(qc)::value, 1024u>(rsrc, cp_lane, slot_addr + (uint32_t)kStageWave * w);
+    else
+      copy_block<decltype(qc)::value>(rsrc, cp_lane, slot_addr + 1024u * w);
   };
   auto copy_chunk = [&](const Chunk& c, uint32_t slot_addr) {
     const __amdgpu_buffer_rsrc_t rsrc = copy_rsrc(c);
-    static_for<0, kCopiesW>([&](auto qc) { copy_one(rsrc, slot_addr, qc); });
+    static_for<0, kCopies>([&](auto qc) { copy_one(rsrc, slot_addr, qc); });
+  };
+  // fp8 cache: the wave's token octet of a staged chunk to bf16 in a chunk
+  // slot (every E4M3 value is exact in bf16; the cache's scale is applied to
+  // the scores and the output instead).  Piece c (16 elements) of token a
+  // becomes bf16 chunks 2 (c % 4) and 2 (c % 4) + 1 of column block c / 4.
+  auto convert_chunk = [&](uint32_t stage_off, uint32_t slot_off) {
+    const int tk = 8 * w + (lane >> 3), j = lane & 7, sw = swz(tk);
+    lds_u8* src = launder(lds + stage_off + (uint32_t)kStageWave * w + 16u * (uint32_t)lane);
+    lds_u8* dst = launder(lds + slot_off + 128u * (uint32_t)tk);
+    static_for<0, kCopies8>([&](auto ic) {
+      constexpr int I = decltype(ic)::value;
+      if (I < kCopies8 - 1 || j < 4) {
+        const u32x4 v = *(const lds_u32x4*)(src + 1024 * I);
+        const int c = 8 * I + j, h = 2 * (c & 3);
+        const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.f, false);
+        const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.f, true);
+        const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.f, false);
+        const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.f, true);
+        const auto p4 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[2], 1.f, false);
+        const auto p5 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[2], 1.f, true);
+        const auto p6 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[3], 1.f, false);
+        const auto p7 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[3], 1.f, true);
+        const uint32_t blk = 4096u * (uint32_t)(c >> 2);
+        *(lds_bf16x8*)(dst + blk + 16u * (uint32_t)(h ^ sw)) =
+            bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        *(lds_bf16x8*)(dst + blk + 16u * (uint32_t)((h + 1) ^ sw)) =
+            bf16x8{p4[0], p4[1], p5[0], p5[1], p6[0], p6[1], p7[0], p7[1]};
+      }
+    });
   };
 
   // ---- state
@@ -498,7 +553,7 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
       score_mfma1(s, kf[k % R], qf[k], k == 0);
       // the copies go out over the first half of the score product (each one as
       // early as the MFMAs allow, so more of the chunk is in flight)
-      if constexpr (WC && k % 2 == 1 && k < 2 * kCopiesW) copy_one(rsrc, cc_slot, std::integral_constant<int, k / 2>{});
+      if constexpr (WC && k % 2 == 1 && k < 2 * kCopies) copy_one(rsrc, cc_slot, std::integral_constant<int, k / 2>{});
       __builtin_amdgcn_sched_barrier(0);
     });
   };
@@ -575,7 +630,7 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
       if (D.last) {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(lsum), __float_as_int(lsum), false, false);
         const float l = __int_as_float(sw[0]) + __int_as_float(sw[1]);
-        cap_inv = l > 0.f ? 1.f / l : 0.f;
+        cap_inv = l > 0.f ? a.kv_scale / l : 0.f;  // (an fp8 cache's V is its bytes times kv_scale)
         cap_lse = l > 0.f ? (m_ref + __builtin_amdgcn_logf(l)) * kLn2 : -INFINITY;
       }
     }
@@ -672,7 +727,9 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
   };
 
   // ---- prologue: the first descriptor batch, copies of chunks 0 and 1, the
-  // queries of the first segment
+  // queries of the first segment.  With an fp8 cache: chunks 0 and 1 copied
+  // to staging, chunk 0 converted to its bf16 slot, chunk 2 copied (it lands
+  // during step -1, which converts chunk 1).
   BatchPos bpos;
   bpos.seq = pi.seq_begin;
   bpos.chunk = 2 * pi.page_begin;
@@ -681,29 +738,57 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
   int c0 = 0;  // chunk ordinal of the batch's first descriptor
   Chunk D0 = unpack_chunk(i32x4{-1, 0, 0, -1});  // chunk t: values
   Chunk D1 = batch_get(batch, 0);                // chunk t + 1: scores
-  Chunk D2 = batch_get(batch, 1);                // chunk t + 2: landing
-  Chunk D3 = batch_get(batch, 2);                // chunk t + 3: copied this step
-  copy_chunk(D1, lds_addr);
-  copy_chunk(D2, lds_addr + kTileBytes);
-  if (D1.valid()) load_queries(D1);
-  queries_ready();
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  Chunk D2 = batch_get(batch, 1);                // chunk t + 2: landing (fp8: converted this step)
+  Chunk D3 = batch_get(batch, 2);                // chunk t + 3: copied this step (fp8: in flight)
+  Chunk D4 = KV8 ? batch_get(batch, 3) : D3;     // fp8: chunk t + 4, copied this step
+  // fp8: bf16 slots of chunks t, t + 1, t + 2 (rotating) and the staging
+  // slot of chunks t + 2 and t + 4 (alternating with that of t + 3)
+  const uint32_t stage_base = (uint32_t)kSlots8 * kTileBytes;
+  uint32_t bs0 = 2 * kTileBytes, bs1 = 0, bs2 = kTileBytes;
+  if constexpr (KV8) {
+    if (D1.valid()) load_queries(D1);
+    copy_chunk(D1, lds_addr + stage_base);
+    copy_chunk(D2, lds_addr + stage_base + kStageBytes);
+    queries_ready();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    convert_chunk(stage_base, 0);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    copy_chunk(D3, lds_addr + stage_base);
+    __syncthreads();
+  } else {
+    copy_chunk(D1, lds_addr);
+    copy_chunk(D2, lds_addr + kTileBytes);
+    if (D1.valid()) load_queries(D1);
+    queries_ready();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
 
   for (int t = -1;; ++t) {
     if (!D0.valid() && !D1.valid()) break;
     const bool v_has = D0.valid() && D0.tok > 0;
     const bool s_has = D1.valid() && D1.tok > 0;
-    const uint32_t slot0 = (uint32_t)(t & 3) * kTileBytes;
-    const uint32_t slot1 = (uint32_t)((t + 1) & 3) * kTileBytes;
-    const uint32_t slot3 = lds_addr + (uint32_t)((t + 3) & 3) * kTileBytes;
+    uint32_t slot0, slot1, slot3;  // (slot3: where this step's copies go)
+    if constexpr (KV8) {
+      slot0 = bs0;
+      slot1 = bs1;
+      const uint32_t stage = stage_base + (uint32_t)(t & 1) * kStageBytes;  // chunks t + 2, t + 4
+      convert_chunk(stage, bs2);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      slot3 = lds_addr + stage;
+    } else {
+      slot0 = (uint32_t)(t & 3) * kTileBytes;
+      slot1 = (uint32_t)((t + 1) & 3) * kTileBytes;
+      slot3 = lds_addr + (uint32_t)((t + 3) & 3) * kTileBytes;
+    }
+    const Chunk& Dc = KV8 ? D4 : D3;  // the chunk this step copies
 
     // the common step: full chunks inside one segment, no limit reached, no
     // pending rescale -- no segment bookkeeping, no masking, no results
     const bool fast = t >= 0 && v_has && D1.valid() && D1.tok == kChunk && !D0.first && !D0.last && !D0.bad &&
                       !D1.first && !D1.last && !pending && kChunk * (D1.chunk + 1) <= lim_min;
     if (fast) {
-      score_loop(slot1, std::true_type{}, D3, slot3);
+      score_loop(slot1, std::true_type{}, Dc, slot3);
       value_loop(slot0, std::integral_constant<int, 2>{}, D1);
     } else {
       // the values enter a new segment / close one
@@ -740,41 +825,63 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
         if (D0.valid() && D0.last) segment_end(D0);
         queries_ready();
         if (s_has)
-          score_loop(slot1, std::false_type{}, D3, slot3);
+          score_loop(slot1, std::false_type{}, Dc, slot3);
         else
           s = f32x16{};
         static_for<0, 2 * kColTiles>([&](auto qc) { smax_piece(qc, D1, std::false_type{}); });
-        copy_chunk(D3, slot3);
+        copy_chunk(Dc, slot3);
       } else {
-        if (s_has) {
-          score_loop(slot1, std::true_type{}, D3, slot3);
-        } else {
-          copy_chunk(D3, slot3);
+        // A step that closes a segment issues its copies after the segment's
+        // stores: stores count in the same vector memory counter, so copies
+        // issued before them would have to land by this step's end.
+        const bool closes = D0.valid() && D0.last;
+        if (s_has && !closes)
+          score_loop(slot1, std::true_type{}, Dc, slot3);
+        else if (s_has)
+          score_loop(slot1, std::false_type{}, Dc, slot3);
+        else
           s = f32x16{};
-        }
+        if (!s_has && !closes) copy_chunk(Dc, slot3);
         if (v_has)
           value_loop(slot0, std::integral_constant<int, 1>{}, D1);
         else if (D1.valid())
           static_for<0, 2 * kColTiles>([&](auto qc) { smax_piece(qc, D1, std::false_type{}); });
-        if (D0.valid() && D0.last) segment_end(D0);
+        if (closes) {
+          segment_end(D0);
+          copy_chunk(Dc, slot3);
+        }
       }
     }
 
-    // ---- end of step: this wave's share of chunk t + 2 has landed (that of
-    // chunk t + 3, the last nine vector memory loads issued, may still be in
-    // flight; loads complete in order)
-    static_assert(kCopiesW == 9, "vmcnt below");
-    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    // ---- end of step: this wave's share of chunk t + 2 (fp8: t + 3) has
+    // landed (that of the chunk copied this step, the last vector memory loads
+    // issued, may still be in flight; loads complete in order)
+    static_assert(kCopiesW == 9 && kCopies8 == 5, "vmcnt below");
+    if constexpr (KV8)
+      asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
     block_sync();
     D0 = D1;
     D1 = D2;
     D2 = D3;
-    // the descriptor of chunk t + 4 (a new batch every 64 chunks)
-    if (t + 4 - c0 >= 64) {
+    if constexpr (KV8) {
+      D3 = D4;
+      const uint32_t b = bs0;
+      bs0 = bs1;
+      bs1 = bs2;
+      bs2 = b;
+    }
+    // the descriptor of the chunk copied next step (a new batch every 64 chunks)
+    constexpr int kAhead = KV8 ? 5 : 4;
+    if (t + kAhead - c0 >= 64) {
       batch = desc_batch(a, pi, bpos, lane);
       c0 += 64;
     }
-    D3 = batch_get(batch, t + 4 - c0);
+    if constexpr (KV8)
+      D4 = batch_get(batch, t + kAhead - c0);
+    else
+      D3 = batch_get(batch, t + kAhead - c0);
   }
 }
 
@@ -782,7 +889,10 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
 
 hipError_t launch_decode_wide(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)(a.num_parts * a.row_blocks));
-  hipLaunchKernelGGL(decode_wide_kernel, grid, dim3(kThreadsW), 0, stream, a);
+  if (a.kv8)
+    hipLaunchKernelGGL(decode_wide_kernel<true>, grid, dim3(kThreadsW), 0, stream, a);
+  else
+    hipLaunchKernelGGL(decode_wide_kernel<false>, grid, dim3(kThreadsW), 0, stream, a);
   return hipGetLastError();
 }
 

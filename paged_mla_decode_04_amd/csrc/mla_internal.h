@@ -16,7 +16,9 @@ struct DecodeArgs {
   int32_t max_blocks;
   const int32_t* seqlens;
   int32_t batch, s_q, h_q, rows, causal;
-  float scale_log2;            // softmax_scale * log2(e)
+  float scale_log2;            // softmax_scale * log2(e) (* kv_scale for an fp8 cache)
+  int32_t kv8;                 // the cache holds E4M3 bytes (the wide kernel converts them to bf16)
+  float kv_scale;              // value of a cache element per unit of its stored number (1 for bf16)
   const int32_t* tile_md;
   const int32_t* num_splits;
   int32_t num_parts, row_blocks;

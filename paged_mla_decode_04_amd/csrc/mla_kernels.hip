@@ -917,7 +917,7 @@ hipError_t launch_plan(const int32_t* seqlens, int batch, int rows, int num_part
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)(a.num_parts * a.row_blocks));
   const int rpb = rows_per_block(a.rows);
-  if (rpb == kRowsPerWorkgroup) return launch_decode_wide(a, stream);
+  if (rpb == kRowsPerWorkgroup || a.kv8) return launch_decode_wide(a, stream);
   if (rpb == 16)
     hipLaunchKernelGGL((decode_kernel<1>), grid, dim3(kThreads), 0, stream, a);
   else if (rpb == 32)
@@ -928,7 +928,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream) {
-  if (rows_per_block(a.rows) == kRowsPerWorkgroup) {
+  if (rows_per_block(a.rows) == kRowsPerWorkgroup || a.kv8) {
     // many splits per sequence on average (a few long sequences over many
     // parts): spread each row tile's splits over four waves as well
     const bool many = (int64_t)a.num_parts + a.batch >= (int64_t)8 * a.batch;

@@ -45,17 +45,19 @@ def test_params_struct_layout_matches(lib):
 
 def test_header_constants_match_binding():
     text = open(HEADER).read()
-    consts = dict(re.findall(r"#define (MLA_[A-Z_]+) (\d+)", text))
+    consts = dict(re.findall(r"#define (MLA_[A-Z0-9_]+) (\d+)", text))
     assert int(consts["MLA_TILE_MD_INTS"]) == _lib.TILE_MD_INTS
     assert int(consts["MLA_ROWS_PER_WORKGROUP"]) == _lib.ROWS_PER_WORKGROUP
     assert int(consts["MLA_MAX_ROWS"]) == _lib.MAX_ROWS
+    assert int(consts["MLA_KV_BF16"]) == _lib.KV_BF16
+    assert int(consts["MLA_KV_FP8_E4M3"]) == _lib.KV_FP8_E4M3
     codes = dict(re.findall(r"(MLA_(?:OK|ERR_[A-Z_]+)) = (\d+)", text))
     for k, v in codes.items():
         assert getattr(_lib, k) == int(v), k
 
 
 def test_status_strings(lib):
-    for s in range(8):
+    for s in range(9):
         assert lib.mla_status_string(s)
     assert lib.mla_status_string(99) == b"unknown status"
 
@@ -111,6 +113,16 @@ BAD = [
     ("blocks overlap", dict(k_block_stride=63 * 576), _lib.MLA_ERR_BAD_STRIDE),
     ("plan without parts", dict(num_parts=0), _lib.MLA_ERR_BAD_SHAPE),
     ("workspace too small", dict(workspace_bytes=1024), _lib.MLA_ERR_WORKSPACE_TOO_SMALL),
+    ("unknown cache type", dict(kv_dtype=2), _lib.MLA_ERR_BAD_ARGUMENT),
+    ("fp8 without a scale", dict(kv_dtype=_lib.KV_FP8_E4M3, kv_scale=0.0), _lib.MLA_ERR_BAD_ARGUMENT),
+    ("fp8 negative scale", dict(kv_dtype=_lib.KV_FP8_E4M3, kv_scale=-1.0), _lib.MLA_ERR_BAD_ARGUMENT),
+    ("fp8 nan scale", dict(kv_dtype=_lib.KV_FP8_E4M3, kv_scale=float("nan")), _lib.MLA_ERR_BAD_ARGUMENT),
+    ("fp8 inf scale", dict(kv_dtype=_lib.KV_FP8_E4M3, kv_scale=float("inf")), _lib.MLA_ERR_BAD_ARGUMENT),
+    # an fp8 row is 1 byte per element: the pitch must be a multiple of 16 bytes
+    ("fp8 pitch 584", dict(kv_dtype=_lib.KV_FP8_E4M3, kv_scale=0.5, k_row_stride=584,
+                            k_block_stride=64 * 584), _lib.MLA_ERR_BAD_STRIDE),
+    ("fp8 block stride", dict(kv_dtype=_lib.KV_FP8_E4M3, kv_scale=0.5, k_block_stride=64 * 576 + 8),
+     _lib.MLA_ERR_BAD_STRIDE),
 ]
 
 

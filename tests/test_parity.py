@@ -26,7 +26,7 @@ from conftest import bits
 from oracle import mla_ref
 from paged_mla_decode_04_amd import (get_mla_metadata, mla_decode_with_kvcache, plan_host,
                                      default_num_parts)
-from paged_mla_decode_04_amd.workloads import D_V, WORKLOADS, Workload, draw
+from paged_mla_decode_04_amd.workloads import D_V, FP8_KV_SCALE, WORKLOADS, Workload, draw
 
 pytestmark = pytest.mark.gpu
 
@@ -45,17 +45,26 @@ def run_gpu(inp, num_parts=None, use_metadata=True, dev="cuda:0"):
     meta = None
     if use_metadata:
         meta = get_mla_metadata(g.cache_seqlens, w.s_q * w.h_q, w.h_kv, num_parts=num_parts)
+    fp8 = w.kv_format == "fp8_e4m3"
     out, lse = mla_decode_with_kvcache(g.q, g.blocked_k, g.block_table, g.cache_seqlens, D_V,
                                        w.softmax_scale, w.causal, metadata=meta,
-                                       num_parts=num_parts)
+                                       num_parts=num_parts, kv_scale=w.kv_scale if fp8 else None)
     torch.cuda.synchronize()
     return out.cpu(), lse.cpu(), meta
 
 
+def cache_raw(inp):
+    """The cache storage as the oracle reads it: bf16 bits or E4M3 bytes."""
+    if inp.kv_format == "fp8_e4m3":
+        return inp.k_storage.numpy()
+    return bits(inp.k_storage)
+
+
 def oracle(inp, batch_indices=None):
-    return mla_ref.mla_decode_ref(bits(inp.q), bits(inp.k_storage), inp.block_table.numpy(),
+    return mla_ref.mla_decode_ref(bits(inp.q), cache_raw(inp), inp.block_table.numpy(),
                                   inp.cache_seqlens.numpy(), inp.softmax_scale, inp.causal,
-                                  batch_indices=batch_indices)
+                                  batch_indices=batch_indices, kv_format=inp.kv_format,
+                                  kv_scale=inp.kv_scale)
 
 
 def assert_parity(out, lse, ref_out, ref_lse, rows=None, what=""):
@@ -300,3 +309,71 @@ def test_random_shapes(seed):
     out, lse, _ = run_gpu(inp, num_parts=parts)
     ref_out, ref_lse = oracle(inp)
     assert_parity(out, lse, ref_out, ref_lse, what=f"random {seed}")
+
+
+# ------------------------------------------------------------- FP8 E4M3 cache
+
+FP8_SMALL = [
+    # (seqlens, s_q, h_q, causal, pitch, parts)
+    ((37, 130), 1, 16, False, 576, None),
+    ((1, 64, 65, 200), 2, 16, True, 640, 5),
+    ((300, 7, 129), 1, 128, False, 576, 3),
+    ((513, 64, 2), 2, 128, True, 640, 7),
+    ((129, 300, 64, 5), 1, 256, False, 576, 6),
+    ((90, 33, 1000), 2, 64, True, 576, 4),
+    ((0, 1, 63, 64, 65, 127, 128, 129), 2, 32, True, 640, 3),
+]
+
+
+@pytest.mark.parametrize("case", FP8_SMALL, ids=[f"fp8_small{i}" for i in range(len(FP8_SMALL))])
+def test_fp8_cache_small_cases(case):
+    lens, s_q, h_q, causal, pitch, parts = case
+    w = Workload("fp8small", batch=len(lens), s_q=s_q, h_q=h_q, causal=causal, seqlens="fixed",
+                 fixed_seqlens=lens, pitch=pitch, kv_format="fp8_e4m3", kv_scale=FP8_KV_SCALE)
+    inp = draw(w, seed=len(lens) * 1000 + h_q, poison=True)
+    note(f"[parity] fp8 small {case}")
+    out, lse, _ = run_gpu(inp, num_parts=parts)
+    ref_out, ref_lse = oracle(inp)
+    assert_parity(out, lse, ref_out, ref_lse, what=f"fp8 {case}")
+
+
+@pytest.mark.parametrize("name", ["wide", "mtp"])
+def test_fp8_cache_full_size(name):
+    """The wide-head and two-token workloads with their cache stored as E4M3 bytes
+    (same shapes, lengths and pages), every sequence against the oracle."""
+    base = WORKLOADS[name]
+    w = Workload(**{**base.__dict__, "name": name + "_fp8", "kv_format": "fp8_e4m3",
+                    "kv_scale": FP8_KV_SCALE})
+    note(f"[parity] fp8 workload {name}: drawing inputs")
+    inp = draw(w)
+    out, lse, _ = run_gpu(inp)
+    note(f"[parity] fp8 workload {name}: oracle on all {w.batch} sequences")
+    ref_out, ref_lse = oracle(inp)
+    worst = assert_parity(out, lse, ref_out, ref_lse, what=f"fp8 {name}")
+    note(f"[parity] fp8 workload {name}: worst out error {worst:.3f} of the bound")
+
+
+def test_fp8_single_token_returns_every_code_exactly():
+    """One cached token whose 576 bytes run through every finite E4M3 code: out is
+    its first 512 values times the scale, exactly (each is a bf16 number)."""
+    w = Workload("fp8codes", batch=1, s_q=1, h_q=16, causal=False, seqlens="fixed",
+                 fixed_seqlens=(1,), kv_format="fp8_e4m3", kv_scale=0.5)
+    inp = draw(w, seed=3)
+    finite = [c for c in range(256) if c not in (0x7F, 0xFF)]
+    row = torch.tensor((finite * 3)[:576], dtype=torch.uint8)
+    inp.k_storage[int(inp.block_table[0, 0]), 0, 0, :576] = row
+    out, lse, _ = run_gpu(inp, num_parts=1)
+    ref_out, ref_lse = oracle(inp)
+    assert np.array_equal(out.float().numpy().astype(np.float64), ref_out)
+    assert np.all(np.abs(lse.numpy() - ref_lse) <= LSE_TOL)
+
+
+def test_fp8_scale_folds_into_scores_and_output():
+    """kv_scale s on the GPU equals the decode at kv_scale 1 with softmax_scale * s,
+    times s (the oracle's closed form, now on the HIP path)."""
+    w = Workload("fp8scale", batch=2, s_q=1, h_q=128, causal=False, seqlens="fixed",
+                 fixed_seqlens=(700, 90), kv_format="fp8_e4m3", kv_scale=0.25)
+    inp = draw(w, seed=12)
+    a_out, a_lse, _ = run_gpu(inp, num_parts=3)
+    ref_out, ref_lse = oracle(inp)
+    assert_parity(a_out, a_lse, ref_out, ref_lse, what="fp8 scale 0.25")
