@@ -35,7 +35,7 @@ from paged_mla_decode_04_amd import traffic
 from paged_mla_decode_04_amd import (_lib, default_num_parts, get_mla_metadata,  # noqa: E402
                                      mla_decode_with_kvcache, workspace_size)
 from paged_mla_decode_04_amd import metrics  # noqa: E402
-from paged_mla_decode_04_amd.workloads import D_V, WORKLOADS, draw  # noqa: E402
+from paged_mla_decode_04_amd.workloads import D_V, FP8_KV_SCALE, WORKLOADS, draw  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
 BF16_PEAK_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, 2.5 PFLOP/s
@@ -63,6 +63,9 @@ def parse():
     ap.add_argument("--s-q", type=int, default=None, help="query tokens per sequence")
     ap.add_argument("--h-q", type=int, default=None, help="query heads")
     ap.add_argument("--causal", choices=("yes", "no"), default=None)
+    ap.add_argument("--kv", choices=("bf16", "fp8"), default="bf16",
+                    help="cache element type: bf16, or E4M3 bytes times a per-cache scale "
+                         "(the byte count then takes one byte per cached element)")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step (plan + decode) in a HIP graph and time its replays "
                          "(removes the host's launch overhead, which small workloads feel)")
@@ -98,6 +101,10 @@ def chosen_workload(args):
     if args.causal is not None and (args.causal == "yes") != w.causal:
         changes["causal"] = args.causal == "yes"
         tags.append("causal" if args.causal == "yes" else "non-causal")
+    if args.kv == "fp8":
+        changes["kv_format"] = "fp8_e4m3"
+        changes["kv_scale"] = FP8_KV_SCALE
+        tags.append("fp8 cache (E4M3 bytes, scale 1/64)")
     if not changes:
         return w
     return dataclasses.replace(w, name=w.name + "+" + "+".join(t.split()[0] for t in tags),
@@ -146,19 +153,23 @@ def cpu_baseline(inp, budget_s: float):
     def raw(t):
         return t.contiguous().view(torch.int16).numpy().view(np.uint16)
 
-    qb, kb = raw(inp.q), raw(inp.k_storage)
+    fp8 = inp.kv_format == "fp8_e4m3"
+    qb = raw(inp.q)
+    kb = inp.k_storage.contiguous().numpy() if fp8 else raw(inp.k_storage)
     bt, sl = inp.block_table.numpy(), inp.cache_seqlens.numpy()
     w = inp.workload
     done, elapsed = [], 0.0
     for b in range(w.batch):
         t0 = time.perf_counter()
-        mla_ref.mla_decode_ref(qb, kb, bt, sl, w.softmax_scale, w.causal, batch_indices=[b])
+        mla_ref.mla_decode_ref(qb, kb, bt, sl, w.softmax_scale, w.causal, batch_indices=[b],
+                               kv_format=inp.kv_format, kv_scale=inp.kv_scale)
         elapsed += time.perf_counter() - t0
         done.append(b)
         if elapsed >= budget_s:
             break
     tokens = int(sl[done].sum())
-    nbytes = metrics.decode_bytes(tokens, len(done), w.s_q, w.h_q, w.h_kv)
+    nbytes = metrics.workload_cost(sl[done].tolist(), len(done), w.s_q, w.h_q, w.h_kv,
+                                   1 if fp8 else 2)["bytes"]
     flops = metrics.decode_flops(w.s_q, tokens, w.h_q)
     threads = None
     try:
@@ -199,12 +210,13 @@ def main():
     lse = torch.empty((b, w.s_q, w.h_q), dtype=torch.float32, device=dev)
     ws = torch.empty((workspace_size(b, w.s_q, w.h_q, w.h_kv, D_V, parts),), dtype=torch.uint8,
                      device=dev)
+    kv_scale = w.kv_scale if w.kv_format == "fp8_e4m3" else None
 
     def step():
         meta = get_mla_metadata(inp.cache_seqlens, rows, w.h_kv, num_parts=parts)
         mla_decode_with_kvcache(inp.q, inp.blocked_k, inp.block_table, inp.cache_seqlens, D_V,
                                 w.softmax_scale, w.causal, metadata=meta, out=out, lse=lse,
-                                workspace=ws)
+                                workspace=ws, kv_scale=kv_scale)
         return meta
 
     for _ in range(args.warmup):
@@ -244,7 +256,7 @@ def main():
             e1.record()
             mla_decode_with_kvcache(inp.q, inp.blocked_k, inp.block_table, inp.cache_seqlens, D_V,
                                     w.softmax_scale, w.causal, metadata=meta, out=out, lse=lse,
-                                    workspace=ws)
+                                    workspace=ws, kv_scale=kv_scale)
             e2.record()
         torch.cuda.synchronize()
         wall_ms = (time.perf_counter() - t0) * 1e3
@@ -275,7 +287,8 @@ def main():
     dec_avg = main_t["decode_ms"]
 
     seqlens = inp_host.cache_seqlens
-    cost = metrics.workload_cost(seqlens.tolist(), b, w.s_q, w.h_q, w.h_kv)
+    cost = metrics.workload_cost(seqlens.tolist(), b, w.s_q, w.h_q, w.h_kv,
+                                 1 if w.kv_format == "fp8_e4m3" else 2)
     gbs = metrics.gbps(cost["bytes"], ms_per_step)
     tfl = metrics.tflops(cost["flops"], ms_per_step)
     achieved = metrics.gbps(cost["bytes"], dec_avg)
@@ -297,6 +310,7 @@ def main():
             "workload": f"{w.name}: {w.description}",
             "batch": b, "s_q": w.s_q, "h_q": w.h_q, "h_kv": w.h_kv, "d": 576, "dv": 512,
             "block_size": 64, "entry_pitch": w.pitch, "block_table": w.table, "causal": w.causal,
+            "cache_dtype": "fp8_e4m3" if w.kv_format == "fp8_e4m3" else "bf16",
             "caches": "flushed before each step" if cold else "warm",
             "launch": "HIP graph replay" if args.graph else "eager",
             "total_seqlens": cost["total_seqlens"], "num_parts": parts,

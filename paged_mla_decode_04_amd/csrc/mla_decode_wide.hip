@@ -726,10 +726,37 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
     asm volatile("s_nop 4" ::: "memory");
   };
 
-  // ---- prologue: the first descriptor batch, copies of chunks 0 and 1, the
-  // queries of the first segment.  With an fp8 cache: chunks 0 and 1 copied
-  // to staging, chunk 0 converted to its bf16 slot, chunk 2 copied (it lands
-  // during step -1, which converts chunk 1).
+  // ---- prologue.  The copies of the part's first two chunks need only the
+  // first sequence's length and the table entry of its first page: both are
+  // loaded (scalar) together with that sequence's queries right after the
+  // part record, and the copies go out before the lane-parallel descriptor
+  // batch is built (its two dependent loads then overlap the copies).  A first
+  // segment of one chunk copies its second chunk from the batch instead.
+  // With an fp8 cache: chunks 0 and 1 copied to staging, chunk 0 converted to
+  // its bf16 slot, chunk 2 copied (it lands during step -1, which converts
+  // chunk 1).
+  const int seq0 = pi.seq_begin;
+  const int n0 = clamp_len(a, load_len(a, seq0));
+  const int phys0 = load_phys(a, seq0, pi.page_begin);
+  auto early_chunk = [&](int chunk) -> Chunk {
+    int tok = n0 - kChunk * chunk;
+    tok = tok < 0 ? 0 : (tok > kChunk ? kChunk : tok);
+    const bool bad = tok > 0 && !(phys0 >= 0 && phys0 < a.num_blocks);
+    return Chunk{seq0, chunk, tok, phys0, false, false, bad};
+  };
+  // (the same range rule as the batch walk: the part's end, one chunk at least)
+  int hi0 = chunk_count(n0);
+  if (seq0 == pi.seq_last && 2 * pi.page_end < hi0) hi0 = 2 * pi.page_end;
+  if (hi0 <= 2 * pi.page_begin) hi0 = 2 * pi.page_begin + 1;
+  const bool second_early = 2 * pi.page_begin + 1 < hi0;
+  const Chunk E1 = early_chunk(2 * pi.page_begin), E2 = early_chunk(2 * pi.page_begin + 1);
+  const uint32_t stage_base = (uint32_t)kSlots8 * kTileBytes;
+  const uint32_t first_dst = KV8 ? lds_addr + stage_base : lds_addr;
+  const uint32_t second_dst = KV8 ? lds_addr + stage_base + kStageBytes : lds_addr + kTileBytes;
+  copy_chunk(E1, first_dst);
+  if (second_early) copy_chunk(E2, second_dst);
+  load_queries(E1);
+
   BatchPos bpos;
   bpos.seq = pi.seq_begin;
   bpos.chunk = 2 * pi.page_begin;
@@ -741,28 +768,18 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
   Chunk D2 = batch_get(batch, 1);                // chunk t + 2: landing (fp8: converted this step)
   Chunk D3 = batch_get(batch, 2);                // chunk t + 3: copied this step (fp8: in flight)
   Chunk D4 = KV8 ? batch_get(batch, 3) : D3;     // fp8: chunk t + 4, copied this step
+  if (!second_early) copy_chunk(D2, second_dst);
   // fp8: bf16 slots of chunks t, t + 1, t + 2 (rotating) and the staging
   // slot of chunks t + 2 and t + 4 (alternating with that of t + 3)
-  const uint32_t stage_base = (uint32_t)kSlots8 * kTileBytes;
   uint32_t bs0 = 2 * kTileBytes, bs1 = 0, bs2 = kTileBytes;
+  queries_ready();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if constexpr (KV8) {
-    if (D1.valid()) load_queries(D1);
-    copy_chunk(D1, lds_addr + stage_base);
-    copy_chunk(D2, lds_addr + stage_base + kStageBytes);
-    queries_ready();
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     convert_chunk(stage_base, 0);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     copy_chunk(D3, lds_addr + stage_base);
-    __syncthreads();
-  } else {
-    copy_chunk(D1, lds_addr);
-    copy_chunk(D2, lds_addr + kTileBytes);
-    if (D1.valid()) load_queries(D1);
-    queries_ready();
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
   }
+  __syncthreads();
 
   for (int t = -1;; ++t) {
     if (!D0.valid() && !D1.valid()) break;

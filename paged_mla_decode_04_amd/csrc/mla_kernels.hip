@@ -613,10 +613,52 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   if (lane == 0) a.lse[(int64_t)b * a.l_sb + (int64_t)qi * a.l_ss + (int64_t)h * a.l_sh] = L;
 }
 
-// The same merge for the wide kernel's fp16 tile partials: one workgroup per
-// (sequence, 32-row tile); wave v merges column tiles 4 v .. 4 v + 3 of the
-// 32 rows in the accumulator layout the partials keep, then the tile goes
-// through LDS so that every output row is written as one 1 KB store.
+// The merges of the wide kernel's fp16 tile partials run in one pass over
+// the splits, online: a running maximum m of the lse seen so far, the sum of
+// exp(lse_i - m) and the sum of exp(lse_i - m) * scale_i * O_i, both rescaled
+// when m grows; out = (weighted sum) / (sum of weights), lse = m + log(sum).
+// Many splits' loads go out together, so that a row's merge takes a round
+// trip to memory per batch of splits, not per split.  An empty partial
+// (lse = -inf) weighs nothing; a row with only empty partials gets out = 0
+// and lse = -inf; a NaN partial lse makes the row's out and lse NaN.
+struct OnlineLse {
+  float m = -INFINITY, sum = 0.f;
+  bool nan = false;
+  // Folds a batch of lse values in; returns the factor the running sums were
+  // scaled by and leaves the batch's weights exp(x - m) in x.
+  template <int B>
+  __device__ __forceinline__ float fold(float (&x)[B]) {
+    float mn = m;
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      if (x[u] != x[u]) nan = true;
+      else mn = fmaxf(mn, x[u]);
+    }
+    const float f = (m == -INFINITY || mn == -INFINITY) ? (mn == -INFINITY ? 1.f : 0.f)
+                                                        : __builtin_amdgcn_exp2f((m - mn) * kLog2e);
+    sum *= f;
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const float w = (x[u] == -INFINITY || x[u] != x[u]) ? 0.f : __builtin_amdgcn_exp2f((x[u] - mn) * kLog2e);
+      sum += w;
+      x[u] = w;
+    }
+    m = mn;
+    return f;
+  }
+  __device__ __forceinline__ float lse() const {
+    if (nan) return __builtin_nanf("");
+    return m == -INFINITY ? -INFINITY : m + __builtin_amdgcn_logf(sum) * kLn2;
+  }
+};
+
+constexpr int kTileMergeBatch = 4;    // splits whose loads are in flight together (tile merge)
+constexpr int kSplitMergeBatch = 8;   // ... per wave (split-parallel merge)
+
+// Few splits per sequence: one workgroup per (sequence, 32-row tile); wave v
+// merges column tiles 4 v .. 4 v + 3 of the 32 rows in the accumulator layout
+// the partials keep, then the tile goes through LDS so that every output row
+// is written as one 1 KB store.
 __global__ __launch_bounds__(256) void combine_tiles_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[32][kDv + 8];
   const int b = blockIdx.x, rt = blockIdx.y;
@@ -627,58 +669,45 @@ __global__ __launch_bounds__(256) void combine_tiles_kernel(DecodeArgs a) {
   const int j = lane & 31, h = lane >> 5;
   const int row = 32 * rt + j;
   const bool ok = row < a.rows;
-  // this lane's row: L = log sum exp(lse_i) (NaN if any partial is NaN), in
-  // one pass (online max and sum) with four loads in flight
   const float* lse_p = a.part_lse + (int64_t)base * a.rows + row;
-  float mx = -INFINITY, sum = 0.f;
-  bool nan = false;
-  for (int i0 = 0; i0 < ns; i0 += kMergeUnroll) {
-    float x[kMergeUnroll];
-#pragma unroll
-    for (int u = 0; u < kMergeUnroll; ++u) x[u] = (ok && i0 + u < ns) ? lse_p[(int64_t)(i0 + u) * a.rows] : -INFINITY;
-#pragma unroll
-    for (int u = 0; u < kMergeUnroll; ++u) {
-      if (x[u] != x[u]) {
-        nan = true;
-      } else if (x[u] > mx) {
-        sum = sum * __builtin_amdgcn_exp2f((mx - x[u]) * kLog2e) + 1.f;
-        mx = x[u];
-      } else if (x[u] != -INFINITY) {
-        sum += __builtin_amdgcn_exp2f((x[u] - mx) * kLog2e);
-      }
-    }
-  }
-  const float L = mx == -INFINITY ? -INFINITY : mx + __builtin_amdgcn_logf(sum) * kLn2;
+  const float* scale_p = a.part_scale + (int64_t)base * a.rows + row;
+  const uint8_t* src0 = (const uint8_t*)a.part_o + (int64_t)base * partial_slot_bytes(a.rows) +
+                        (int64_t)rt * kPartialTileBytes + 8 * 1024 * v + 16 * lane;
   float acc[8][8];
 #pragma unroll
   for (int p = 0; p < 8; ++p)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[p][e] = 0.f;
-  if (L != -INFINITY && !nan) {
-    const uint8_t* src0 = (const uint8_t*)a.part_o + (int64_t)base * partial_slot_bytes(a.rows) +
-                          (int64_t)rt * kPartialTileBytes + 8 * 1024 * v + 16 * lane;
-    const float* scale_p = a.part_scale + (int64_t)base * a.rows + row;
-    for (int i = 0; i < ns; ++i) {
-      const float x = ok ? lse_p[(int64_t)i * a.rows] : -INFINITY;
-      // the split's weight, times its row's power-of-two factor (an empty split weighs nothing)
-      const float wgt = x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((x - L) * kLog2e) * scale_p[(int64_t)i * a.rows];
-      const uint8_t* src = src0 + (int64_t)i * partial_slot_bytes(a.rows);
+  OnlineLse ol;
+  for (int i0 = 0; i0 < ns; i0 += kTileMergeBatch) {
+    float x[kTileMergeBatch], sc[kTileMergeBatch];
+    f16x8 pv[kTileMergeBatch][8];
 #pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        const f16x8 pv = *(const f16x8*)(src + 1024 * p);
+    for (int u = 0; u < kTileMergeBatch; ++u) {
+      const int i = i0 + u;
+      const bool in = i < ns;
+      x[u] = (in && ok) ? lse_p[(int64_t)i * a.rows] : -INFINITY;
+      sc[u] = (in && ok) ? scale_p[(int64_t)i * a.rows] : 0.f;
+      const uint8_t* src = src0 + (int64_t)(in ? i : 0) * partial_slot_bytes(a.rows);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[p][e] += wgt * (float)pv[e];
-      }
+      for (int p = 0; p < 8; ++p) pv[u][p] = in ? *(const f16x8*)(src + 1024 * p) : f16x8{};
     }
-  }
-  float Lo = L;
-  if (nan) {
-    Lo = __builtin_nanf("");
+    const float f = ol.fold(x);
 #pragma unroll
     for (int p = 0; p < 8; ++p)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[p][e] = __builtin_nanf("");
+      for (int e = 0; e < 8; ++e) acc[p][e] *= f;
+#pragma unroll
+    for (int u = 0; u < kTileMergeBatch; ++u) {
+      const float wgt = x[u] * sc[u];
+#pragma unroll
+      for (int p = 0; p < 8; ++p)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[p][e] += wgt * (float)pv[u][p][e];
+    }
   }
+  const float Lo = ol.lse();
+  const float inv = (ol.nan || !(ol.sum > 0.f)) ? (ol.nan ? __builtin_nanf("") : 0.f) : 1.f / ol.sum;
   // pair p of wave v: column tile ct = 4 v + (p >> 1), elements of g = 2 (p & 1) + (e >> 2)
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
@@ -688,7 +717,7 @@ __global__ __launch_bounds__(256) void combine_tiles_kernel(DecodeArgs a) {
       const int col = 32 * ct + 8 * (2 * (p & 1) + gg) + 4 * h;
       bf16x4 o4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o4[e] = (__bf16)acc[p][4 * gg + e];
+      for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[p][4 * gg + e] * inv);
       *(bf16x4*)&tile[j][col] = o4;
     }
   }
@@ -709,138 +738,92 @@ __global__ __launch_bounds__(256) void combine_tiles_kernel(DecodeArgs a) {
   }
 }
 
-// The same merge for sequences split many ways (a few long sequences over
-// many parts).  Workgroup (b, rt, ct) merges column tile ct (32 columns) of
-// row tile rt (32 rows) of sequence b over all its splits:
-//   1. L = log sum_i exp(lse_i) per row, each row's splits spread over eight
-//      threads (online max and sum, four loads in flight), then merged;
-//   2. wave v accumulates splits v, v + 4, ... weighted by exp(lse_i - L),
-//      four splits' loads in flight per lane;
-//   3. the four waves' sums are added through LDS and written as 32 rows of
-//      64 contiguous bytes, lse by the workgroup of column tile 0.
-// A row whose partials are all -inf gets out = 0 and lse = -inf; a NaN
-// partial lse makes the row's out and lse NaN.
+// Many splits per sequence (a few long sequences over many parts): workgroup
+// (b, rt, ct) merges column tile ct (32 columns) of row tile rt (32 rows) of
+// sequence b.  Wave v folds splits v, v + 4, ... online, eight splits' loads
+// at a time; the four waves' running sums are then combined through LDS and
+// written as 32 rows of 64 contiguous bytes, lse by column tile 0.
 __global__ __launch_bounds__(256) void combine_splits_kernel(DecodeArgs a) {
-  __shared__ float s_m[8][32], s_s[8][32];
-  __shared__ int s_nan[8][32];
-  __shared__ float s_L[32];
+  __shared__ float red_m[4][64], red_s[4][64];
+  __shared__ int red_nan[4][64];
   __shared__ float red[4][64][16];
   const int b = blockIdx.x, rt = blockIdx.y, ct = blockIdx.z;
-  const int v = threadIdx.x >> 6;
+  const int v = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int base = a.num_splits[b];
   const int ns = a.num_splits[b + 1] - base;
   if (ns <= 1) return;
   const int t = threadIdx.x;
-  const float* lse_p = a.part_lse + (int64_t)base * a.rows + 32 * rt;
   {
-    // 1. this thread's share of row j's splits: i = sub, sub + 8, ...
-    const int j = t & 31, sub = t >> 5;
+    const int j = lane & 31;
     const bool ok = 32 * rt + j < a.rows;
-    float m = -INFINITY, sum = 0.f;
-    bool nan = false;
-    for (int i0 = sub; i0 < ns; i0 += 8 * kMergeUnroll) {
-      float x[kMergeUnroll];
-#pragma unroll
-      for (int u = 0; u < kMergeUnroll; ++u) {
-        const int i = i0 + 8 * u;
-        x[u] = (ok && i < ns) ? lse_p[(int64_t)i * a.rows + j] : -INFINITY;
-      }
-#pragma unroll
-      for (int u = 0; u < kMergeUnroll; ++u) {
-        if (x[u] != x[u]) {
-          nan = true;
-        } else if (x[u] > m) {
-          sum = sum * __builtin_amdgcn_exp2f((m - x[u]) * kLog2e) + 1.f;
-          m = x[u];
-        } else if (x[u] != -INFINITY) {
-          sum += __builtin_amdgcn_exp2f((x[u] - m) * kLog2e);
-        }
-      }
-    }
-    s_m[sub][j] = m;
-    s_s[sub][j] = sum;
-    s_nan[sub][j] = nan;
-  }
-  __syncthreads();
-  if (t < 32) {
-    float m = -INFINITY;
-    bool nan = false;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      m = fmaxf(m, s_m[k][t]);
-      nan |= s_nan[k][t] != 0;
-    }
-    float L = -INFINITY;
-    if (m != -INFINITY) {
-      float sum = 0.f;
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        if (s_m[k][t] != -INFINITY) sum += s_s[k][t] * __builtin_amdgcn_exp2f((s_m[k][t] - m) * kLog2e);
-      L = m + __builtin_amdgcn_logf(sum) * kLn2;
-    }
-    s_L[t] = nan ? __builtin_nanf("") : L;
-  }
-  __syncthreads();
-  {
-    // 2. wave v: splits v, v + 4, ...
-    const int lane = t & 63, j = lane & 31;
-    const bool ok = 32 * rt + j < a.rows;
-    const float L = s_L[j];
+    const float* lse_p = a.part_lse + (int64_t)base * a.rows + 32 * rt + j;
+    const float* scale_p = a.part_scale + (int64_t)base * a.rows + 32 * rt + j;
+    const uint8_t* src0 = (const uint8_t*)a.part_o + (int64_t)base * partial_slot_bytes(a.rows) +
+                          (int64_t)rt * kPartialTileBytes + 2048 * ct + 16 * lane;
     float acc[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-    if (ok && L != -INFINITY && L == L) {
-      const uint8_t* src0 = (const uint8_t*)a.part_o + (int64_t)base * partial_slot_bytes(a.rows) +
-                            (int64_t)rt * kPartialTileBytes + 2048 * ct + 16 * lane;
-      const float* scale_p = a.part_scale + (int64_t)base * a.rows + 32 * rt + j;
-      for (int i0 = v; i0 < ns; i0 += 4 * kMergeUnroll) {
-        float x[kMergeUnroll], sc[kMergeUnroll];
-        f16x8 d[kMergeUnroll][2];
+    OnlineLse ol;
+    for (int i0 = v; i0 < ns; i0 += 4 * kSplitMergeBatch) {
+      float x[kSplitMergeBatch], sc[kSplitMergeBatch];
+      f16x8 d[kSplitMergeBatch][2];
 #pragma unroll
-        for (int u = 0; u < kMergeUnroll; ++u) {
-          const int i = i0 + 4 * u;
-          if (i < ns) {
-            x[u] = lse_p[(int64_t)i * a.rows + j];
-            sc[u] = scale_p[(int64_t)i * a.rows];
-            const uint8_t* src = src0 + (int64_t)i * partial_slot_bytes(a.rows);
-            d[u][0] = *(const f16x8*)src;
-            d[u][1] = *(const f16x8*)(src + 1024);
-          } else {
-            x[u] = -INFINITY;
-            sc[u] = 0.f;
-            d[u][0] = d[u][1] = f16x8{};
-          }
-        }
+      for (int u = 0; u < kSplitMergeBatch; ++u) {
+        const int i = i0 + 4 * u;
+        const bool in = i < ns;
+        x[u] = (in && ok) ? lse_p[(int64_t)i * a.rows] : -INFINITY;
+        sc[u] = (in && ok) ? scale_p[(int64_t)i * a.rows] : 0.f;
+        const uint8_t* src = src0 + (int64_t)(in ? i : 0) * partial_slot_bytes(a.rows);
+        d[u][0] = in ? *(const f16x8*)src : f16x8{};
+        d[u][1] = in ? *(const f16x8*)(src + 1024) : f16x8{};
+      }
+      const float f = ol.fold(x);
 #pragma unroll
-        for (int u = 0; u < kMergeUnroll; ++u) {
-          // the split's weight, times its row's power-of-two factor (an empty split weighs nothing)
-          const float wgt = x[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((x[u] - L) * kLog2e) * sc[u];
+      for (int e = 0; e < 16; ++e) acc[e] *= f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            acc[e] += wgt * (float)d[u][0][e];
-            acc[8 + e] += wgt * (float)d[u][1][e];
-          }
+      for (int u = 0; u < kSplitMergeBatch; ++u) {
+        const float wgt = x[u] * sc[u];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          acc[e] += wgt * (float)d[u][0][e];
+          acc[8 + e] += wgt * (float)d[u][1][e];
         }
       }
     }
+    red_m[v][lane] = ol.m;
+    red_s[v][lane] = ol.sum;
+    red_nan[v][lane] = ol.nan;
 #pragma unroll
     for (int e = 0; e < 16; ++e) red[v][lane][e] = acc[e];
   }
   __syncthreads();
   {
-    // 3. row j = t / 8, output columns 4 c .. 4 c + 3 of the tile; column i
-    // of the tile is accumulator 4 (i / 8) + i % 4 of lane j + 32 ((i / 4) % 2)
+    // row j = t / 8, output columns 4 c .. 4 c + 3 of the tile; column i of
+    // the tile is accumulator 4 (i / 8) + i % 4 of lane j + 32 ((i / 4) % 2)
     const int j = t >> 3, c = t & 7;
     const int row = 32 * rt + j;
-    const float L = s_L[j];
+    float M = -INFINITY;
+    bool nan = false;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      M = fmaxf(M, red_m[w][j]);
+      nan |= red_nan[w][j] != 0;
+    }
+    float wv[4], S = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      wv[w] = (M == -INFINITY || red_m[w][j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((red_m[w][j] - M) * kLog2e);
+      S += wv[w] * red_s[w][j];
+    }
+    const float inv = nan ? __builtin_nanf("") : (S > 0.f ? 1.f / S : 0.f);
+    const float L = nan ? __builtin_nanf("") : (M == -INFINITY ? -INFINITY : M + __builtin_amdgcn_logf(S) * kLn2);
     bf16x4 o4;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 4 * c + e;
       const int ln = j + 32 * ((i >> 2) & 1), r = 4 * (i >> 3) + (i & 3);
-      float val = red[0][ln][r] + red[1][ln][r] + red[2][ln][r] + red[3][ln][r];
-      if (L != L) val = __builtin_nanf("");
-      o4[e] = (__bf16)val;
+      const float val = wv[0] * red[0][ln][r] + wv[1] * red[1][ln][r] + wv[2] * red[2][ln][r] + wv[3] * red[3][ln][r];
+      o4[e] = (__bf16)(val * inv);
     }
     if (row < a.rows) {
       const int qi = row / a.h_q, hh = row - qi * a.h_q;

@@ -54,10 +54,14 @@ def blocks_after_alignment(blocks: int, entry_elems: int = D_QK, elem_bytes: int
     return blocks * entry_elems // padded
 
 
-def workload_cost(seqlens, b: int, s_q: int, h_q: int, h_kv: int = 1):
+def workload_cost(seqlens, b: int, s_q: int, h_q: int, h_kv: int = 1, cache_elem_bytes: int = 2):
+    """FLOPs and bytes of one call.  With an fp8 cache (cache_elem_bytes 1) the
+    cache term counts one byte per element and the query and output terms stay
+    bf16: the same formula with each term at its own element size."""
     total = int(sum(int(x) for x in seqlens))
+    qo = decode_bytes(0, b, s_q, h_q, h_kv)
     return {
         "total_seqlens": total,
         "flops": decode_flops(s_q, total, h_q),
-        "bytes": decode_bytes(total, b, s_q, h_q, h_kv),
+        "bytes": qo + int(total) * h_kv * D_QK * int(cache_elem_bytes),
     }
