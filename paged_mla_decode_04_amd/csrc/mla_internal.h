@@ -44,6 +44,11 @@ __host__ __device__ inline int64_t partial_slot_bytes(int rows) {
   return (int64_t)((rows + 31) / 32) * kPartialTileBytes;
 }
 
+// The tile merge reads a sequence's splits one batch after another; when the
+// splits per sequence average seven or more (a few long sequences over many
+// parts), the split-parallel merge spreads them over four waves instead.
+inline bool many_splits(int64_t num_parts, int64_t batch) { return num_parts + batch >= 8 * batch; }
+
 hipError_t launch_plan(const int32_t* seqlens, int batch, int rows, int num_parts, int32_t* tile_md,
                        int32_t* num_splits, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

@@ -35,7 +35,7 @@
 // (4 tokens x 2 chunks x 2 halves per 16 lanes) free of bank conflicts.
 #include <utility>
 
-#include "mla_device.h"
+#include "mla_merge.h"
 
 namespace mla {
 
@@ -613,129 +613,14 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   if (lane == 0) a.lse[(int64_t)b * a.l_sb + (int64_t)qi * a.l_ss + (int64_t)h * a.l_sh] = L;
 }
 
-// The merges of the wide kernel's fp16 tile partials run in one pass over
-// the splits, online: a running maximum m of the lse seen so far, the sum of
-// exp(lse_i - m) and the sum of exp(lse_i - m) * scale_i * O_i, both rescaled
-// when m grows; out = (weighted sum) / (sum of weights), lse = m + log(sum).
-// Many splits' loads go out together, so that a row's merge takes a round
-// trip to memory per batch of splits, not per split.  An empty partial
-// (lse = -inf) weighs nothing; a row with only empty partials gets out = 0
-// and lse = -inf; a NaN partial lse makes the row's out and lse NaN.
-struct OnlineLse {
-  float m = -INFINITY, sum = 0.f;
-  bool nan = false;
-  // Folds a batch of lse values in; returns the factor the running sums were
-  // scaled by and leaves the batch's weights exp(x - m) in x.
-  template <int B>
-  __device__ __forceinline__ float fold(float (&x)[B]) {
-    float mn = m;
-#pragma unroll
-    for (int u = 0; u < B; ++u) {
-      if (x[u] != x[u]) nan = true;
-      else mn = fmaxf(mn, x[u]);
-    }
-    const float f = (m == -INFINITY || mn == -INFINITY) ? (mn == -INFINITY ? 1.f : 0.f)
-                                                        : __builtin_amdgcn_exp2f((m - mn) * kLog2e);
-    sum *= f;
-#pragma unroll
-    for (int u = 0; u < B; ++u) {
-      const float w = (x[u] == -INFINITY || x[u] != x[u]) ? 0.f : __builtin_amdgcn_exp2f((x[u] - mn) * kLog2e);
-      sum += w;
-      x[u] = w;
-    }
-    m = mn;
-    return f;
-  }
-  __device__ __forceinline__ float lse() const {
-    if (nan) return __builtin_nanf("");
-    return m == -INFINITY ? -INFINITY : m + __builtin_amdgcn_logf(sum) * kLn2;
-  }
-};
-
-constexpr int kTileMergeBatch = 4;    // splits whose loads are in flight together (tile merge)
-constexpr int kSplitMergeBatch = 8;   // ... per wave (split-parallel merge)
-
-// Few splits per sequence: one workgroup per (sequence, 32-row tile); wave v
-// merges column tiles 4 v .. 4 v + 3 of the 32 rows in the accumulator layout
-// the partials keep, then the tile goes through LDS so that every output row
-// is written as one 1 KB store.
+// Few splits per sequence: one workgroup per (sequence, 32-row tile).
 __global__ __launch_bounds__(256) void combine_tiles_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[32][kDv + 8];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[32 * kMergeTileStride];
   const int b = blockIdx.x, rt = blockIdx.y;
   const int base = a.num_splits[b];
   const int ns = a.num_splits[b + 1] - base;
   if (ns <= 1) return;
-  const int v = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int j = lane & 31, h = lane >> 5;
-  const int row = 32 * rt + j;
-  const bool ok = row < a.rows;
-  const float* lse_p = a.part_lse + (int64_t)base * a.rows + row;
-  const float* scale_p = a.part_scale + (int64_t)base * a.rows + row;
-  const uint8_t* src0 = (const uint8_t*)a.part_o + (int64_t)base * partial_slot_bytes(a.rows) +
-                        (int64_t)rt * kPartialTileBytes + 8 * 1024 * v + 16 * lane;
-  float acc[8][8];
-#pragma unroll
-  for (int p = 0; p < 8; ++p)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[p][e] = 0.f;
-  OnlineLse ol;
-  for (int i0 = 0; i0 < ns; i0 += kTileMergeBatch) {
-    float x[kTileMergeBatch], sc[kTileMergeBatch];
-    f16x8 pv[kTileMergeBatch][8];
-#pragma unroll
-    for (int u = 0; u < kTileMergeBatch; ++u) {
-      const int i = i0 + u;
-      const bool in = i < ns;
-      x[u] = (in && ok) ? lse_p[(int64_t)i * a.rows] : -INFINITY;
-      sc[u] = (in && ok) ? scale_p[(int64_t)i * a.rows] : 0.f;
-      const uint8_t* src = src0 + (int64_t)(in ? i : 0) * partial_slot_bytes(a.rows);
-#pragma unroll
-      for (int p = 0; p < 8; ++p) pv[u][p] = in ? *(const f16x8*)(src + 1024 * p) : f16x8{};
-    }
-    const float f = ol.fold(x);
-#pragma unroll
-    for (int p = 0; p < 8; ++p)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[p][e] *= f;
-#pragma unroll
-    for (int u = 0; u < kTileMergeBatch; ++u) {
-      const float wgt = x[u] * sc[u];
-#pragma unroll
-      for (int p = 0; p < 8; ++p)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[p][e] += wgt * (float)pv[u][p][e];
-    }
-  }
-  const float Lo = ol.lse();
-  const float inv = (ol.nan || !(ol.sum > 0.f)) ? (ol.nan ? __builtin_nanf("") : 0.f) : 1.f / ol.sum;
-  // pair p of wave v: column tile ct = 4 v + (p >> 1), elements of g = 2 (p & 1) + (e >> 2)
-#pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const int ct = 4 * v + (p >> 1);
-#pragma unroll
-    for (int gg = 0; gg < 2; ++gg) {
-      const int col = 32 * ct + 8 * (2 * (p & 1) + gg) + 4 * h;
-      bf16x4 o4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[p][4 * gg + e] * inv);
-      *(bf16x4*)&tile[j][col] = o4;
-    }
-  }
-  if (v == 0 && h == 0 && ok) {
-    const int qi = row / a.h_q, hh = row - qi * a.h_q;
-    a.lse[(int64_t)b * a.l_sb + (int64_t)qi * a.l_ss + (int64_t)hh * a.l_sh] = Lo;
-  }
-  __syncthreads();
-  // wave v writes rows 8 v .. 8 v + 7, 64 lanes x 16 bytes each
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const int jr = 8 * v + r, orow = 32 * rt + jr;
-    if (orow < a.rows) {
-      const int qi = orow / a.h_q, hh = orow - qi * a.h_q;
-      uint16_t* op = a.out + (int64_t)b * a.o_sb + (int64_t)qi * a.o_ss + (int64_t)hh * a.o_sh + 8 * lane;
-      *(bf16x8*)op = *(const bf16x8*)&tile[jr][8 * lane];
-    }
-  }
+  merge_row_tile(a, b, rt, base, ns, (lds_u16*)tile);
 }
 
 // Many splits per sequence (a few long sequences over many parts): workgroup
@@ -912,10 +797,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
 
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream) {
   if (rows_per_block(a.rows) == kRowsPerWorkgroup || a.kv8) {
-    // many splits per sequence on average (a few long sequences over many
-    // parts): spread each row tile's splits over four waves as well
-    const bool many = (int64_t)a.num_parts + a.batch >= (int64_t)8 * a.batch;
-    if (many) {
+    if (many_splits(a.num_parts, a.batch)) {
       const dim3 grid((unsigned)a.batch, (unsigned)((a.rows + 31) / 32), (unsigned)(kDv / 32));
       hipLaunchKernelGGL(combine_splits_kernel, grid, dim3(256), 0, stream, a);
     } else {

@@ -184,6 +184,29 @@ def test_device_plan_equals_host_plan():
         assert torch.equal(md.cpu(), hmd) and torch.equal(ns.cpu(), hns), name
 
 
+def test_one_plan_serves_consecutive_calls():
+    """One plan serves several calls in a row (one per layer of a decode
+    step), each exact, and no call changes it."""
+    w = Workload("layers", batch=6, s_q=2, h_q=128, causal=True, seqlens="fixed",
+                 fixed_seqlens=(900, 64, 2100, 1, 333, 1500))
+    parts = 9  # every long sequence split in two or three
+    meta = None
+    for layer in range(3):
+        inp = draw(w, seed=20 + layer)
+        g = inp.to("cuda:0")
+        if meta is None:
+            meta = get_mla_metadata(g.cache_seqlens, w.s_q * w.h_q, w.h_kv, num_parts=parts)
+            host_md, host_ns = plan_host(inp.cache_seqlens, w.s_q * w.h_q, w.h_kv, parts)
+        note(f"[parity] one plan, call {layer}")
+        out, lse = mla_decode_with_kvcache(g.q, g.blocked_k, g.block_table, g.cache_seqlens, D_V,
+                                           w.softmax_scale, w.causal, metadata=meta)
+        torch.cuda.synchronize()
+        ref_out, ref_lse = oracle(inp)
+        assert_parity(out.cpu(), lse.cpu(), ref_out, ref_lse, what=f"call {layer}")
+        md = meta[0].cpu()
+        assert torch.equal(md, host_md) and torch.equal(meta[1].cpu(), host_ns), "plan changed"
+
+
 def test_page_permutation_is_bit_identical():
     w = Workload("perm", batch=3, s_q=2, h_q=64, causal=True, seqlens="fixed",
                  fixed_seqlens=(700, 64, 333))
