@@ -11,7 +11,9 @@ import os
 import threading
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmla_decode.so")
+# (MLA_DECODE_LIBRARY names another build of the same library, such as the
+# sanitized host build the CPU tests load)
+LIB_PATH = os.environ.get("MLA_DECODE_LIBRARY") or os.path.join(HERE, "libmla_decode.so")
 
 MLA_OK = 0
 MLA_ERR_NULL_POINTER = 1

@@ -193,5 +193,60 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+# A copy of the library whose host code runs under AddressSanitizer and
+# UndefinedBehaviorSanitizer (the device code is built as usual): the host-side
+# argument checks, the host planner and the status strings then run with every
+# out-of-bounds access, use after free and undefined operation reported.  Run a
+# CPU test against it with the sanitizer runtime preloaded (asan_runtime()).
+SANITIZE_FLAGS = "-Xarch_host -fsanitize=address,undefined -Xarch_host -fno-omit-frame-pointer -Xarch_host -fno-sanitize-recover=undefined".split()
+SANITIZED_DIR = os.path.join(os.path.dirname(HERE), "_build", "sanitized")
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's shared AddressSanitizer runtime."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    r = subprocess.run([os.path.join(rocm, "llvm", "bin", "clang"), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    path = r.stdout.decode().strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError(f"no AddressSanitizer runtime found ({path!r})")
+    return path
+
+
+def build_sanitized() -> str:
+    """Build the sanitized copy into _build/sanitized (skipped when it is newer than every source)."""
+    out = os.path.join(SANITIZED_DIR, LIB_NAME)
+    srcs = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".h"))]
+    srcs.append(os.path.join(os.path.dirname(HERE), "include", "mla_decode.h"))
+    if os.path.exists(out) and os.path.getmtime(out) > max(os.path.getmtime(f) for f in srcs):
+        return out
+    os.makedirs(SANITIZED_DIR, exist_ok=True)
+    flags = [f for f in HIPCC_FLAGS if f != "-O3"] + ["-O1", "-g"] + SANITIZE_FLAGS
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = os.path.join(SANITIZED_DIR, src.replace(".hip", ".o"))
+        cmd = [hipcc(), *flags, "-c", os.path.join(CSRC, src), "-o", obj]
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+        objs.append(obj)
+    failed = []
+    for src, p in procs:
+        text, _ = p.communicate()
+        if p.returncode != 0:
+            failed.append(f"{src}:\n{text.decode(errors='replace')}")
+    if failed:
+        raise RuntimeError("hipcc (sanitized host code) failed:\n" + "\n".join(failed))
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *SANITIZE_FLAGS, *objs, "-o", out + ".tmp"]
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if r.returncode != 0:
+        raise RuntimeError("link (sanitized) failed:\n" + r.stdout.decode(errors="replace"))
+    os.replace(out + ".tmp", out)
+    for o in objs:
+        os.remove(o)
+    return out
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--sanitized" in sys.argv:
+        print(build_sanitized())
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include <atomic>
 #include <mutex>
@@ -216,10 +217,16 @@ mla_status decode_call(const mla_decode_params* p, void* stream, bool no_alloc) 
 
 }  // namespace
 
+static_assert(sizeof(mla_status) == sizeof(int), "mla_status is an int");
+
 extern "C" {
 
 const char* mla_status_string(mla_status status) {
-  switch (status) {
+  // A C caller may pass any int; in C++ reading an enum object outside the
+  // enumerators' range is undefined, so read its bytes as an int instead.
+  int code;
+  memcpy(&code, &status, sizeof code);
+  switch (code) {
     case MLA_OK: return "ok";
     case MLA_ERR_NULL_POINTER: return "a required pointer is NULL";
     case MLA_ERR_BAD_SHAPE: return "invalid or inconsistent size";
