@@ -189,8 +189,9 @@ def cpu_baseline(inp, budget_s: float):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU; multi-GPU runs are not "
-                                   "part of this build", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this benchmark runs on one GPU: the decode path has no "
+                                   "multi-GPU mode (it would shard by sequence, one plan per GPU)",
+                          "n_gpus": args.gpus}))
         sys.exit(2)
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
