@@ -590,7 +590,7 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
 #pragma unroll
       for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
       const bool over = FAST ? mx > kRescaleSlack : (m_ref == -INFINITY ? mx > -INFINITY : mx > kRescaleSlack);
-      if (__builtin_amdgcn_ballot_w64(over) != 0) {
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(over) != 0, 0)) {  // (rare: kept out of line)
         // a chunk max passed the reference by more than 2^16 (or the segment
         // just started): move the row's reference to its max
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(mx), __float_as_int(mx), false, false);
