@@ -41,6 +41,13 @@
 // score reads (32 tokens x one chunk per 512 bytes) and the transposing value
 // reads (4 tokens x 4 chunks per 256 bytes) at two and one pass over the
 // banks.
+//
+// An fp8 cache (one E4M3 byte per element, one scale per cache) takes the
+// same path after a widening step: its chunks (18 KB) are copied as bytes into
+// a staging area, and each step converts the staged chunk t + 2 to bf16 in a
+// chunk slot (three slots) before copying chunk t + 4 into the staging it just
+// read.  Every E4M3 value is exact in bf16; the cache's scale multiplies the
+// score scale and the output's 1 / l instead of every element.
 #include <type_traits>
 
 #include "mla_device.h"
@@ -670,8 +677,8 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
   };
 
   // ---- the end of chunk D0's segment: this wave's rows of out and lse, or,
-  // for a split sequence, its bf16 partial (O / l) and lse; then clear the
-  // accumulators.  The partial of a split keeps the accumulator layout: per
+  // for a split sequence, its fp16 partial (O / l, scaled per row) and lse;
+  // then clear the accumulators.  The partial of a split keeps the accumulator layout: per
   // 32-row tile, tile ct and element pair gp, 64 lanes x 16 bytes (elements
   // 8 gp .. 8 gp + 7 of the lane's 16), so every store is 1 KB contiguous.
   auto segment_end = [&](const Chunk& D0) {
