@@ -179,11 +179,17 @@ def cpu_baseline(inp, budget_s: float):
     except Exception:
         threads = os.cpu_count()
     ms = elapsed * 1e3
+    cpu = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), cpu)
+    except OSError:
+        pass
     return {"value": round(metrics.gbps(nbytes, ms), 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "tflops": round(metrics.tflops(flops, ms), 6),
             "seconds": round(elapsed, 3),
             "sample": f"{len(done)} of {w.batch} sequences ({tokens} cached tokens), fp64 NumPy "
-                      f"oracle, {os.cpu_count()} host cores visible"}
+                      f"oracle, {os.cpu_count()} host cores visible ({cpu})"}
 
 
 def main():
