@@ -400,3 +400,37 @@ def test_fp8_scale_folds_into_scores_and_output():
     a_out, a_lse, _ = run_gpu(inp, num_parts=3)
     ref_out, ref_lse = oracle(inp)
     assert_parity(a_out, a_lse, ref_out, ref_lse, what="fp8 scale 0.25")
+
+
+def _fp8_inputs(lens, s_q, h_q, causal, seed):
+    w = Workload("fp8inv", batch=len(lens), s_q=s_q, h_q=h_q, causal=causal, seqlens="fixed",
+                 fixed_seqlens=lens, kv_format="fp8_e4m3", kv_scale=FP8_KV_SCALE)
+    return draw(w, seed=seed)
+
+
+def test_fp8_page_permutation_and_pitch_are_bit_identical():
+    """With an fp8 cache, moving the pages (and the table with them) and storing
+    the entries at a 640-byte pitch change no bit of the results."""
+    inp = _fp8_inputs((700, 64, 333), 2, 128, True, seed=14)
+    a_out, a_lse, _ = run_gpu(inp, num_parts=4)
+    nb = inp.k_storage.shape[0]
+    perm = torch.randperm(nb, generator=torch.Generator().manual_seed(15))
+    moved = inp.k_storage.clone()
+    moved[perm] = inp.k_storage
+    padded = torch.full(moved.shape[:-1] + (640,), 0x7F, dtype=torch.uint8)  # E4M3 NaN bytes
+    padded[..., :576] = moved
+    inp.k_storage = padded
+    inp.blocked_k = padded[..., :576]
+    inp.block_table = perm[inp.block_table.long()].to(torch.int32)
+    note("[parity] fp8 permuted pages at pitch 640")
+    b_out, b_lse, _ = run_gpu(inp, num_parts=4)
+    assert torch.equal(a_out, b_out) and torch.equal(a_lse, b_lse)
+
+
+@pytest.mark.parametrize("parts", [1, 7, 64, 256])
+def test_fp8_split_count_invariance(parts):
+    inp = _fp8_inputs((3000, 70, 1500), 2, 128, True, seed=16)
+    note(f"[parity] fp8 forced parts {parts}")
+    out, lse, _ = run_gpu(inp, num_parts=parts)
+    ref_out, ref_lse = oracle(inp)
+    assert_parity(out, lse, ref_out, ref_lse, what=f"fp8 parts={parts}")

@@ -62,6 +62,29 @@ def test_no_alloc_equals_workspace_call(pair, with_plan):
         assert torch.equal(l, rl), f"{w.name}: lse differs from the workspace call"
 
 
+def test_no_alloc_fp8_equals_workspace_call():
+    """The same with an fp8 cache (the 128-row kernel with its staging area)."""
+    pair = [Workload("na_fp8", batch=4, s_q=1, h_q=128, causal=False, seqlens="fixed",
+                     fixed_seqlens=(2500, 90, 1200, 1), kv_format="fp8_e4m3", kv_scale=1 / 64),
+            Workload("na_fp8_small", batch=1, s_q=2, h_q=64, causal=True, seqlens="fixed",
+                     fixed_seqlens=(300,), kv_format="fp8_e4m3", kv_scale=1 / 64)]
+    inputs = [draw(w, seed=60 + i, poison=True).to("cuda:0") for i, w in enumerate(pair)]
+
+    def run(g, no_alloc):
+        w = g.workload
+        out, lse = mla_decode_with_kvcache(g.q, g.blocked_k, g.block_table, g.cache_seqlens, D_V,
+                                           w.softmax_scale, w.causal, no_alloc=no_alloc,
+                                           kv_scale=w.kv_scale)
+        torch.cuda.synchronize()
+        return out.cpu(), lse.cpu()
+
+    note("[no-alloc] fp8: workspace calls, then two no-allocation calls")
+    refs = [run(g, False) for g in inputs]
+    got = [run(g, True) for g in inputs]
+    for (ro, rl), (o, l), w in zip(refs, got, pair):
+        assert torch.equal(o, ro) and torch.equal(l, rl), w.name
+
+
 def test_no_alloc_rejects_a_call_beyond_its_scratch():
     """16384 sequences of 1024 rows need far more than the static scratch: the
     call returns MLA_ERR_SCRATCH_TOO_SMALL before enqueueing anything."""
