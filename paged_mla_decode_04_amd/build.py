@@ -146,6 +146,82 @@ def check_mfma_operand_hazards(asm_path: str, src: str) -> None:
         raise RuntimeError(f"{src}: VALU result feeds an MFMA too early: {bad[:4]}")
 
 
+# An LDS-direct load reads M0; after a write of M0 it needs one wait state,
+# which the compiler inserts for the loads it emits itself but not for loads
+# written as inline assembly.  The kernels' copies carry their own s_nop; this
+# check keeps it so.
+LDS_DMA_SOURCES = ["mla_decode_wide.hip", "mla_kernels.hip"]
+_WRITES_M0 = re.compile(r"^[sv]_\w+\s+m0\b")
+
+
+def _instructions(asm_path: str):
+    insts = []    # instruction text, or ("LABEL", name)
+    with open(asm_path) as f:
+        for line in f:
+            code = line.split(";", 1)[0].rstrip()
+            if not code.strip():
+                continue
+            if not code.startswith("\t"):
+                if code.endswith(":"):
+                    insts.append(("LABEL", code[:-1]))
+                continue
+            t = code.strip()
+            if not t.startswith("."):
+                insts.append(t)
+    return insts
+
+
+def check_lds_dma_m0_hazards(asm_path: str, src: str) -> None:
+    """Fail if an LDS-direct load can follow a write of M0 with no wait state between."""
+    insts = _instructions(asm_path)
+    branches = {}
+    for k, t in enumerate(insts):
+        if isinstance(t, str) and (t.startswith("s_cbranch") or t.startswith("s_branch")):
+            branches.setdefault(t.split()[-1], []).append(k)
+    bad = []
+
+    def ends_flow(t) -> bool:
+        return isinstance(t, str) and (t.startswith("s_branch") or t.startswith("s_endpgm")
+                                       or t.startswith("s_setpc"))
+
+    def walk(j: int, load: str, seen: set) -> None:
+        # the instruction right before the load on this path (labels and branches
+        # are not wait states)
+        while j >= 0:
+            pt = insts[j]
+            if isinstance(pt, tuple):
+                for b in branches.get(pt[1], []):
+                    if b not in seen:
+                        seen.add(b)
+                        walk(b - 1, load, seen)
+                if j == 0 or ends_flow(insts[j - 1]):
+                    return
+                j -= 1
+                continue
+            if pt.startswith("s_cbranch") or pt.startswith("s_branch"):
+                j -= 1
+                continue
+            if _WRITES_M0.match(pt):
+                bad.append(f"{pt} -> {load}")
+            return
+
+    for k, t in enumerate(insts):
+        if isinstance(t, str) and t.split()[0].startswith(("buffer_load", "global_load")) and t.endswith(" lds"):
+            walk(k - 1, t, set())
+    if bad:
+        raise RuntimeError(f"{src}: an LDS-direct load follows an M0 write without a wait state: {bad[:4]}")
+
+
+def check_lds_dma(src: str) -> None:
+    with tempfile.TemporaryDirectory() as td:
+        out = os.path.join(td, "k.s")
+        cmd = [hipcc(), *HIPCC_FLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out]
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc -S failed for {src}:\n" + r.stdout.decode(errors="replace"))
+        check_lds_dma_m0_hazards(out, src)
+
+
 def build(verbose: bool = False) -> str:
     objs = []
     procs = []
@@ -173,6 +249,8 @@ def build(verbose: bool = False) -> str:
     try:
         for src in FIXED_AGPR_SOURCES:
             check_fixed_agprs(src)
+        for src in LDS_DMA_SOURCES:
+            check_lds_dma(src)
     except RuntimeError:
         if os.path.exists(LIB_PATH):
             os.remove(LIB_PATH)

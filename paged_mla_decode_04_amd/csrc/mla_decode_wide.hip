@@ -91,10 +91,12 @@ __device__ __forceinline__ int swz(int a) { return (((a >> 1) & 1) << 2) | ((a >
 // added to the LDS address too, so M0 is lowered by it).  A bf16 cache copies
 // column block Q (LSTRIDE 4096, the block's place in a chunk slot), an fp8
 // cache byte range 128 Q .. 128 Q + 127 of each row (LSTRIDE 1024, staging).
+// (The s_nop is the wait state an LDS-direct load needs after the scalar write
+// of M0 just before it; the compiler does not insert it for assembly.)
 template <int Q, uint32_t LSTRIDE = 4096u>
 __device__ __forceinline__ void copy_block(__amdgpu_buffer_rsrc_t rsrc, uint32_t lane_off, uint32_t wave_base) {
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen offset:%2 lds" ::"v"(lane_off), "s"(rsrc), "n"(128 * Q),
-               "{m0}"(wave_base + (LSTRIDE - 128u) * Q)
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen offset:%2 lds" ::"v"(lane_off), "s"(rsrc),
+               "n"(128 * Q), "{m0}"(wave_base + (LSTRIDE - 128u) * Q)
                : "memory");
 }
 

@@ -67,8 +67,13 @@ typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
 // write: it would otherwise make every later LDS read wait for all copies in
 // flight.  Completion is awaited explicitly (vmcnt) before the barrier that
 // hands a chunk over, and a copy only targets a tile no wave reads any more.
+// An LDS-direct load reads M0, which the compiler writes (a scalar
+// instruction) right before the assembly; the load needs one wait state after
+// that write, which the compiler's hazard check does not see through inline
+// assembly, so the s_nop is part of the block.
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr) : "memory");
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr)
+               : "memory");
 }
 // Position of the page-bookkeeping cursor: one 32-token chunk of the part's
 // (sequence, chunk) order.

@@ -1,6 +1,7 @@
-"""The build's check that no VALU result reaches an inline-assembly MFMA operand
-with fewer than two wait states (the compiler's hazard recognizer does not see
-assembly MFMAs), on synthetic assembly."""
+"""The build's hazard checks on synthetic assembly: no VALU result reaches an
+inline-assembly MFMA operand with fewer than two wait states, and no LDS-direct
+load directly follows a write of M0 (the compiler's hazard recognizer does not
+see through inline assembly in either case)."""
 
 import pytest
 
@@ -45,3 +46,35 @@ def test_fall_through_after_an_unconditional_branch_is_not_a_path(tmp_path):
     text = ("\tv_mov_b32 v5, 0\n\ts_branch .LBB0_3\n.LBB0_2:\n\ts_nop 1\n" + MFMA +
             ".LBB0_3:\n\ts_endpgm\n")
     check(tmp_path, text)
+
+
+LDS_LOAD = "\tbuffer_load_dwordx4 v204, s[24:27], 0 offen offset:0x80 lds\n"
+
+
+def check_dma(tmp_path, text):
+    p = tmp_path / "d.s"
+    p.write_text(text)
+    build.check_lds_dma_m0_hazards(str(p), "d")
+
+
+def test_lds_load_right_after_an_m0_write_is_caught(tmp_path):
+    with pytest.raises(RuntimeError):
+        check_dma(tmp_path, "\ts_add_i32 m0, s14, s44\n" + LDS_LOAD)
+    with pytest.raises(RuntimeError):
+        check_dma(tmp_path, "\ts_mov_b32 m0, s6\n" + LDS_LOAD)
+
+
+def test_one_wait_state_after_the_m0_write_is_enough(tmp_path):
+    check_dma(tmp_path, "\ts_add_i32 m0, s14, s44\n\ts_nop 0\n" + LDS_LOAD)
+    check_dma(tmp_path, "\ts_mov_b32 m0, s6\n\tv_lshlrev_b32_e32 v0, 2, v0\n" + LDS_LOAD)
+
+
+def test_m0_write_before_a_branch_into_the_load_is_caught(tmp_path):
+    text = ("\ts_mov_b32 m0, s6\n\ts_cbranch_scc1 .LBB0_2\n\ts_nop 0\n.LBB0_2:\n" + LDS_LOAD)
+    with pytest.raises(RuntimeError):
+        check_dma(tmp_path, text)
+
+
+def test_the_kernels_pass_the_m0_check():
+    for src in build.LDS_DMA_SOURCES:
+        build.check_lds_dma(src)
