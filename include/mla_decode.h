@@ -42,7 +42,8 @@
  * are safe.  Launch failures are reported as MLA_ERR_HIP.
  *
  * Device-side preconditions (not checkable on the host without a copy):
- * cache_seqlens[b] <= max_blocks_per_seq * 64 (larger values are clamped),
+ * 0 <= cache_seqlens[b] <= max_blocks_per_seq * 64 (larger values are clamped
+ * to the table's width, negative ones read as an empty sequence),
  * block_table entries of used pages lie in [0, num_blocks) (a page outside
  * that range is never read; its sequence's rows come out NaN instead), and
  * no input is written while a call that reads it is in flight.

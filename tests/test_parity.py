@@ -315,6 +315,21 @@ def test_lengths_past_the_table_are_clamped(h_q, parts):
     assert_parity(out, lse, ref_out, ref_lse, what=f"clamp h_q={h_q} parts={parts}")
 
 
+@pytest.mark.parametrize("h_q,kv", [(128, "bf16"), (16, "bf16"), (128, "fp8_e4m3")])
+def test_negative_lengths_read_as_empty(h_q, kv):
+    """A negative stored length is an empty sequence (out 0, lse -inf); the
+    sequences around it are unaffected."""
+    w = Workload("neg", batch=3, s_q=2, h_q=h_q, causal=True, seqlens="fixed",
+                 fixed_seqlens=(300, 0, 700), kv_format=kv,
+                 kv_scale=FP8_KV_SCALE if kv == "fp8_e4m3" else 1.0)
+    inp = draw(w, seed=33, poison=True)
+    ref_out, ref_lse = oracle(inp)
+    inp.cache_seqlens = torch.tensor([300, -5, 700], dtype=torch.int32)
+    note(f"[parity] negative length h_q={h_q} {kv}")
+    out, lse, _ = run_gpu(inp, num_parts=5)
+    assert_parity(out, lse, ref_out, ref_lse, what=f"negative length h_q={h_q} {kv}")
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_random_shapes(seed):
     """Seeded random shapes: odd head counts (rows not a multiple of 16 or 32),
