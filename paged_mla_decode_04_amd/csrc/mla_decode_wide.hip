@@ -576,7 +576,16 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
     constexpr int q = decltype(qc)::value;
     constexpr bool FAST = decltype(fast_tag)::value;
     if constexpr (q == 0) {
-      mfma_result_wait();
+      // The scores' last MFMA is followed, in a common step, by the value
+      // product's first fragment reads (2 kVAhead of them, held in place by
+      // the scheduling barriers), their wait and the first value MFMA: with
+      // four more wait states that is past the 18 the result needs.
+      if constexpr (FAST) {
+        static_assert(2 * kVAhead + 2 + 4 >= 18, "wait states before the first score read");
+        asm volatile("s_nop 3" ::: "memory");
+      } else {
+        mfma_result_wait();
+      }
       // (a common step's reference is finite: its segment's first chunk had
       // visible keys in every row)
       mu = FAST ? m_ref : (m_ref == -INFINITY ? 0.f : m_ref);
