@@ -40,7 +40,8 @@ _ASM_AGPR = re.compile(r"accvgpr|\ba\[\d|[ ,]a\d+\b")
 
 
 def check_fixed_agprs(src: str) -> None:
-    """Fail if the compiler itself references AGPRs, or spills VGPRs, in the kernel's assembly."""
+    """Fail if the compiler itself references AGPRs, spills VGPRs or uses scratch memory in the
+    kernel's assembly."""
     with tempfile.TemporaryDirectory() as td:
         out = os.path.join(td, "k.s")
         cmd = [hipcc(), *HIPCC_FLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out]
@@ -64,10 +65,20 @@ def check_fixed_agprs(src: str) -> None:
             raise RuntimeError(f"{src}: the compiler uses AGPRs reserved for the accumulators "
                                f"(register pressure too high?): {bad[:4]}")
         with open(out) as f:
-            spills = [int(m.group(1)) for m in re.finditer(r"\.vgpr_spill_count:\s+(\d+)", f.read())]
-        if any(spills):
-            raise RuntimeError(f"{src}: the compiler spills VGPRs to scratch memory ({spills})")
+            check_no_scratch(f.read(), src)
         check_mfma_operand_hazards(out, src)
+
+
+def check_no_scratch(text: str, src: str) -> None:
+    """Fail if a kernel in the assembly `text` spills VGPRs or uses scratch memory at all: a
+    variable the compiler keeps in memory (an array indexed at run time, or one captured by
+    a call it did not inline) is scratch traffic without a spill."""
+    spills = [int(m.group(1)) for m in re.finditer(r"\.vgpr_spill_count:\s+(\d+)", text)]
+    if any(spills):
+        raise RuntimeError(f"{src}: the compiler spills VGPRs to scratch memory ({spills})")
+    scratch = [int(m.group(1)) for m in re.finditer(r"\.amdhsa_private_segment_fixed_size\s+(\d+)", text)]
+    if any(scratch):
+        raise RuntimeError(f"{src}: the kernel uses scratch memory ({scratch} bytes per lane)")
 
 
 _REG = re.compile(r"([va])\[(\d+):(\d+)\]|([va])(\d+)\b")

@@ -1,7 +1,8 @@
-"""The build's hazard checks on synthetic assembly: no VALU result reaches an
-inline-assembly MFMA operand with fewer than two wait states, and no LDS-direct
+"""The build's checks on synthetic assembly: no VALU result reaches an
+inline-assembly MFMA operand with fewer than two wait states, no LDS-direct
 load directly follows a write of M0 (the compiler's hazard recognizer does not
-see through inline assembly in either case)."""
+see through inline assembly in either case), and no kernel uses scratch
+memory."""
 
 import pytest
 
@@ -78,3 +79,24 @@ def test_m0_write_before_a_branch_into_the_load_is_caught(tmp_path):
 def test_the_kernels_pass_the_m0_check():
     for src in build.LDS_DMA_SOURCES:
         build.check_lds_dma(src)
+
+
+SCRATCH = """\t.amdhsa_kernel k
+\t\t.amdhsa_private_segment_fixed_size {size}
+\t.end_amdhsa_kernel
+\t.vgpr_spill_count: {spills}
+"""
+
+
+def test_scratch_use_without_a_spill_is_caught():
+    with pytest.raises(RuntimeError, match="scratch memory"):
+        build.check_no_scratch(SCRATCH.format(size=192, spills=0), "k")
+
+
+def test_a_spill_is_caught():
+    with pytest.raises(RuntimeError, match="spills"):
+        build.check_no_scratch(SCRATCH.format(size=8, spills=2), "k")
+
+
+def test_no_scratch_passes():
+    build.check_no_scratch(SCRATCH.format(size=0, spills=0), "k")
