@@ -60,9 +60,16 @@ MLA_HD inline int row_blocks(int rows) {
 
 // Fixed cost of one (part, sequence) segment, in pages.  A page is
 // 64 * 576 * 2 = 73728 B of cache; a segment reads rows * 1152 B of queries
-// and writes rows * 1024 B of output, or rows * 2052 B of fp32 partial that
-// the merge reads again (these mostly stay in L2 / the memory-side cache).
+// and writes rows * 1024 B of output, or a partial the merge reads again
+// (rows * 1032 B of fp16 tiles from the wide kernel, rows * 2052 B of fp32
+// from the narrow one), and spends a few steps outside the pipelined loop.
+// For the wide kernel's 128-row blocks, per-workgroup timers at b = 128,
+// h_q = 128, seqlens ~ N(4096, 1024) fit about 3850 cycles per 32-token chunk
+// and 17600 per segment, i.e. 2.3 pages; of charges 2 to 5, 3 gave the
+// shortest calls there and with two query tokens.  The narrow kernel keeps
+// ceil(rows / 28).
 MLA_HD inline int segment_cost(int rows_in_block) {
+  if (rows_in_block >= kRowsPerWorkgroup) return 3;
   const int c = (rows_in_block + 27) / 28;
   return c < 1 ? 1 : c;
 }

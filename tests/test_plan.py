@@ -31,7 +31,7 @@ def units(n):
 
 def seg_cost(q_rows):
     r = 16 if q_rows <= 16 else 32 if q_rows <= 32 else 64 if q_rows <= 64 else 128
-    return max(1, (r + 27) // 28)
+    return 3 if r == 128 else max(1, (r + 27) // 28)
 
 
 def check_plan(seqlens, q_rows, num_parts, md, ns):
