@@ -66,7 +66,55 @@ def check_fixed_agprs(src: str) -> None:
                                f"(register pressure too high?): {bad[:4]}")
         with open(out) as f:
             check_no_scratch(f.read(), src)
+        if src == "mla_decode_wide.hip":
+            check_score_reads_ahead(out, src)
         check_mfma_operand_hazards(out, src)
+
+
+_WIDE_KERNEL = re.compile(r"^_ZN\S*decode_wide_kernel\S*:")
+_SCORE_MFMA = re.compile(r"^\s*v_mfma_f32_32x32x16_bf16 v\[")
+_LGKM = re.compile(r"s_waitcnt\b.*lgkmcnt\((\d+)\)")
+SCORE_STEPS = 36  # score MFMAs per chunk (576 / 16)
+
+
+def check_score_reads_ahead(path: str, src: str) -> None:
+    """Fail if the wide kernel's common-step score product waits for all LDS
+    reads before more than its last MFMA.  Each score MFMA should wait only
+    for the K fragment read a few MFMAs earlier (lgkmcnt(3)); the compiler
+    turns that into a full drain (lgkmcnt(0)) when it believes a scalar load,
+    which shares the counter and returns out of order, may still be in
+    flight -- one change elsewhere in the kernel did exactly that and cost 5%
+    of the compute-bound call.  The common step is found by the short wait
+    that opens its value product (an s_nop 3 in the assembly) and its 36 score
+    MFMAs (the ones writing VGPRs) before it."""
+    with open(path) as f:
+        lines = f.read().split("\n")
+    starts = [i for i, l in enumerate(lines) if _WIDE_KERNEL.match(l)]
+    if not starts:
+        raise RuntimeError(f"{src}: no decode_wide_kernel in the assembly")
+    for start in starts:
+        nop = next((i for i in range(start, len(lines)) if lines[i].strip() == "s_nop 3"), None)
+        if nop is None:
+            raise RuntimeError(f"{src}: common step not found (no s_nop 3 after {lines[start][:60]})")
+        waits, k = [], nop
+        while len(waits) < SCORE_STEPS and k > start:
+            k -= 1
+            if _SCORE_MFMA.match(lines[k]):
+                w = None
+                for j in range(k - 1, max(start, k - 12), -1):
+                    m = _LGKM.search(lines[j])
+                    if m:
+                        w = int(m.group(1))
+                        break
+                    if _SCORE_MFMA.match(lines[j]):
+                        break
+                waits.append(w)
+        if len(waits) < SCORE_STEPS:
+            raise RuntimeError(f"{src}: fewer than {SCORE_STEPS} score MFMAs before the common step's value product")
+        drains = sum(1 for w in waits if w == 0)
+        if drains > 1:
+            raise RuntimeError(f"{src}: {drains} score MFMAs of the common step wait for every LDS read "
+                               f"(lgkmcnt(0)): the reads ahead are lost ({lines[start][:60]})")
 
 
 def check_no_scratch(text: str, src: str) -> None:

@@ -1,8 +1,9 @@
 """The build's checks on synthetic assembly: no VALU result reaches an
 inline-assembly MFMA operand with fewer than two wait states, no LDS-direct
 load directly follows a write of M0 (the compiler's hazard recognizer does not
-see through inline assembly in either case), and no kernel uses scratch
-memory."""
+see through inline assembly in either case), no kernel uses scratch
+memory, and the wide kernel's common-step score product keeps its LDS reads
+ahead (no full LDS wait before any but its last MFMA)."""
 
 import pytest
 
@@ -100,3 +101,34 @@ def test_a_spill_is_caught():
 
 def test_no_scratch_passes():
     build.check_no_scratch(SCRATCH.format(size=0, spills=0), "k")
+
+
+def score_loop(waits):
+    body = ["_ZN3mla12_GLOBAL__N_118decode_wide_kernelILb0EEEvNS_10DecodeArgsE:"]
+    for w in waits:
+        body += ["\tds_read_b128 v[28:31], v191 offset:4096", f"\ts_waitcnt lgkmcnt({w})",
+                 "\t;;#ASMSTART", "\tv_mfma_f32_32x32x16_bf16 v[0:15], v[28:31], v[32:35], v[0:15]", "\t;;#ASMEND"]
+    body += ["\t;;#ASMSTART", "\tv_mfma_f32_32x32x16_bf16 a[0:15], v[12:15], v[170:173], a[0:15]", "\t;;#ASMEND",
+             "\t;;#ASMSTART", "\ts_nop 3", "\t;;#ASMEND"]
+    return "\n".join(body) + "\n"
+
+
+def test_score_reads_ahead_pass():
+    import tempfile, os
+    with tempfile.TemporaryDirectory() as td:
+        p = os.path.join(td, "k.s")
+        open(p, "w").write(score_loop([3] * 33 + [2, 1, 0]))
+        build.check_score_reads_ahead(p, "k")
+
+
+def test_full_lds_waits_in_the_score_loop_are_caught():
+    import tempfile, os
+    with tempfile.TemporaryDirectory() as td:
+        p = os.path.join(td, "k.s")
+        open(p, "w").write(score_loop(([0, 3, 3, 3] * 9)[:33] + [2, 1, 0]))
+        with pytest.raises(RuntimeError, match="reads ahead are lost"):
+            build.check_score_reads_ahead(p, "k")
+
+
+def test_the_wide_kernel_keeps_its_score_reads_ahead():
+    build.check_fixed_agprs("mla_decode_wide.hip")

@@ -271,6 +271,30 @@ def test_growing_scores_exercise_the_rescale(h_q, s_q, causal, parts):
     assert_parity(out, lse, ref_out, ref_lse, what="ramp")
 
 
+@pytest.mark.parametrize("log2_scale", [17, -20])
+def test_split_partials_outside_the_fp16_range(log2_scale):
+    """Split sequences whose weighted values leave fp16's normal range: the
+    cache is scaled by 2^s and the queries by 2^-s (exact in bf16), so every
+    score is unchanged and every O / l is 2^s times the unscaled one -- above
+    fp16's largest value at s = 17, below its smallest normal at s = -20 (the
+    wide kernel rewrites such a partial row with a power-of-two scale).  Both
+    sides are compared at the unscaled magnitude (out / 2^s against ref / 2^s,
+    exact): the bound's floor of 1 is not scale-invariant, and an element that
+    cancels carries an error proportional to its row's scale (P is bf16)."""
+    w = Workload("fp16range", batch=3, s_q=1, h_q=128, causal=False, seqlens="fixed",
+                 fixed_seqlens=(1500, 900, 2100))
+    inp = draw(w, seed=31)
+    f = 2.0 ** log2_scale
+    inp.k_storage.mul_(f)
+    inp.q.mul_(1.0 / f)
+    note(f"[parity] split partials scaled by 2^{log2_scale}")
+    out, lse, _ = run_gpu(inp, num_parts=7)
+    ref_out, ref_lse = oracle(inp)
+    peak = float(np.abs(ref_out).max())
+    assert (peak > 65504.0) if log2_scale > 0 else (peak < 2.0 ** -14)
+    assert_parity(out.float() / f, lse, ref_out / f, ref_lse, what=f"partials x2^{log2_scale}")
+
+
 def test_maximum_rows():
     """s_q * h_q at the library's limit (1024 rows: eight row blocks), causal."""
     w = Workload("maxrows", batch=3, s_q=8, h_q=128, causal=True, seqlens="fixed",
