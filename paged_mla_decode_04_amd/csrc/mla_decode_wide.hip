@@ -744,16 +744,18 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
     asm volatile("s_nop 4" ::: "memory");
   };
 
-  // ---- prologue.  The copies of the part's first two chunks need only the
-  // first sequence's length and the table entry of its first page: both are
-  // loaded (scalar) together with that sequence's queries right after the
-  // part record, and the copies go out before the lane-parallel descriptor
-  // batch is built (its two dependent loads then overlap the copies).  A first
-  // segment of one chunk copies its second chunk from the batch instead.
-  // With an fp8 cache: chunks 0 and 1 copied to staging, chunk 0 converted to
-  // its bf16 slot, chunk 2 copied (it lands during step -1, which converts
-  // chunk 1).
+  // ---- prologue.  The first sequence's queries need only the part record,
+  // so they go out first (all parts start at once, and the queries are most
+  // of the bytes every part needs before its first step).  The copies of the
+  // part's first two chunks need the first sequence's length and the table
+  // entry of its first page (scalar loads issued with the queries), and go
+  // out before the lane-parallel descriptor batch is built (its two dependent
+  // loads then overlap the copies).  A first segment of one chunk copies its
+  // second chunk from the batch instead.  With an fp8 cache: chunks 0 and 1
+  // copied to staging, chunk 0 converted to its bf16 slot, chunk 2 copied (it
+  // lands during step -1, which converts chunk 1).
   const int seq0 = pi.seq_begin;
+  load_queries(Chunk{seq0, 0, 0, 0, false, false, false});
   const int n0 = clamp_len(a, load_len(a, seq0));
   const int phys0 = load_phys(a, seq0, pi.page_begin);
   auto early_chunk = [&](int chunk) -> Chunk {
@@ -773,7 +775,6 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
   const uint32_t second_dst = KV8 ? lds_addr + stage_base + kStageBytes : lds_addr + kTileBytes;
   copy_chunk(E1, first_dst);
   if (second_early) copy_chunk(E2, second_dst);
-  load_queries(E1);
 
   BatchPos bpos;
   bpos.seq = pi.seq_begin;
