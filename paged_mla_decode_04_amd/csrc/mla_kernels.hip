@@ -624,15 +624,19 @@ __global__ __launch_bounds__(256) void combine_tiles_kernel(DecodeArgs a) {
 }
 
 // Many splits per sequence (a few long sequences over many parts): workgroup
-// (b, rt, ct) merges column tile ct (32 columns) of row tile rt (32 rows) of
+// (ct, rt, b) merges column tile ct (32 columns) of row tile rt (32 rows) of
 // sequence b.  Wave v folds splits v, v + 4, ... online, eight splits' loads
 // at a time; the four waves' running sums are then combined through LDS and
-// written as 32 rows of 64 contiguous bytes, lse by column tile 0.
+// written as 32 rows of 64 contiguous bytes, lse by column tile 0.  The
+// sequence is the grid's slowest index, so a sequence's workgroups are
+// dispatched together: with more workgroups than fit at once, a long
+// sequence's (the ones that run longest) then do not wait behind other
+// sequences' tiles.
 __global__ __launch_bounds__(256) void combine_splits_kernel(DecodeArgs a) {
   __shared__ float red_m[4][64], red_s[4][64];
   __shared__ int red_nan[4][64];
   __shared__ float red[4][64][16];
-  const int b = blockIdx.x, rt = blockIdx.y, ct = blockIdx.z;
+  const int ct = blockIdx.x, rt = blockIdx.y, b = blockIdx.z;
   const int v = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int base = a.num_splits[b];
   const int ns = a.num_splits[b + 1] - base;
@@ -798,7 +802,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream) {
   if (rows_per_block(a.rows) == kRowsPerWorkgroup || a.kv8) {
     if (many_splits(a.num_parts, a.batch)) {
-      const dim3 grid((unsigned)a.batch, (unsigned)((a.rows + 31) / 32), (unsigned)(kDv / 32));
+      const dim3 grid((unsigned)(kDv / 32), (unsigned)((a.rows + 31) / 32), (unsigned)a.batch);
       hipLaunchKernelGGL(combine_splits_kernel, grid, dim3(256), 0, stream, a);
     } else {
       const dim3 grid((unsigned)a.batch, (unsigned)((a.rows + 31) / 32));
