@@ -769,7 +769,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* seqlens, int 
   }
   const int64_t T = plan_stride(prefix[batch], num_parts, c);
   for (int p = tid; p < num_parts; p += 1024)
-    plan_part(prefix, seqlens, batch, c, T, p, tile_md + (int64_t)p * kTileMdInts);
+    plan_part(prefix, batch, c, T, p, tile_md + (int64_t)p * kTileMdInts);
   for (int base = 0; base < batch; base += 1024) {
     const int i = base + tid;
     const int32_t v = i < batch ? plan_touches(prefix, i, c, T) : 0;

@@ -99,7 +99,7 @@ MLA_HD inline int locate(const int64_t* prefix, int batch, int64_t x) {
 }
 
 // Part p's record from the prefix sums (prefix has batch + 1 entries).
-MLA_HD inline void plan_part(const int64_t* prefix, const int32_t* seqlens, int batch, int c, int64_t T,
+MLA_HD inline void plan_part(const int64_t* prefix, int batch, int c, int64_t T,
                              int p, int32_t* md) {
   const int64_t W = prefix[batch];
   const int64_t x = (int64_t)p * T;
@@ -114,9 +114,11 @@ MLA_HD inline void plan_part(const int64_t* prefix, const int32_t* seqlens, int 
   const int pg = off > 0 ? (int)off : 0;
   int eb, epg;
   const int64_t xn = x + T;
+  // (sequence e's units are prefix[e + 1] - prefix[e] - c: no second read of
+  // the lengths)
   if (xn >= W) {
     eb = batch - 1;
-    epg = seq_units(seqlens[batch - 1]);
+    epg = (int)(prefix[batch] - prefix[batch - 1] - c);
   } else {
     const int nb = locate(prefix, batch, xn);
     const int64_t noff = xn - prefix[nb] - c;
@@ -125,7 +127,7 @@ MLA_HD inline void plan_part(const int64_t* prefix, const int32_t* seqlens, int 
       epg = (int)noff;
     } else {
       eb = nb - 1;
-      epg = seq_units(seqlens[nb - 1]);
+      epg = (int)(prefix[nb] - prefix[nb - 1] - c);
     }
   }
   md[0] = b;
@@ -148,7 +150,7 @@ inline void plan_split_kv_host(const int32_t* seqlens, int batch, int q_rows_per
   prefix[0] = 0;
   for (int b = 0; b < batch; ++b) prefix[b + 1] = prefix[b] + c + seq_units(seqlens[b]);
   const int64_t T = plan_stride(prefix[batch], num_parts, c);
-  for (int p = 0; p < num_parts; ++p) plan_part(prefix, seqlens, batch, c, T, p, tile_md + (int64_t)p * kTileMdInts);
+  for (int p = 0; p < num_parts; ++p) plan_part(prefix, batch, c, T, p, tile_md + (int64_t)p * kTileMdInts);
   num_splits[0] = 0;
   for (int b = 0; b < batch; ++b) num_splits[b + 1] = num_splits[b] + plan_touches(prefix, b, c, T);
 }
