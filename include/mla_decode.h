@@ -152,8 +152,14 @@ typedef struct mla_decode_params {
   int32_t causal;        /* nonzero: bottom-right causal mask over the s_q query tokens */
 
   /* optional plan from mla_get_metadata for the same seqlens / q_rows / h_kv;
-     NULL tile_md: the call plans internally (into the workspace) with num_parts parts
-     (num_parts <= 0: the device default) */
+     NULL tile_md: the call plans internally with num_parts parts (num_parts <= 0: the
+     device default), and the workspace then starts with that plan: tile_md
+     [num_parts][MLA_TILE_MD_INTS] at byte 0, num_splits [batch + 1] at the next 256-byte
+     boundary.  For a bf16 cache with at most 256 sequences (and a row block of other than
+     64 rows, i.e. s_q * h_q / h_kv not in 33..64) the decode kernels plan for themselves in
+     their first instructions instead of after a separate plan launch; their plan is
+     mla_get_metadata's except that lengths past max_blocks_per_seq * 64 count as that
+     many tokens. */
   const int32_t* tile_md;
   const int32_t* num_splits;
   int32_t num_parts;

@@ -68,6 +68,8 @@ def check_fixed_agprs(src: str) -> None:
             check_no_scratch(f.read(), src)
         if src == "mla_decode_wide.hip":
             check_score_reads_ahead(out, src)
+            with open(out) as f:
+                check_m0_only_in_copies(f.read(), src)
         check_mfma_operand_hazards(out, src)
 
 
@@ -115,6 +117,26 @@ def check_score_reads_ahead(path: str, src: str) -> None:
         if drains > 1:
             raise RuntimeError(f"{src}: {drains} score MFMAs of the common step wait for every LDS read "
                                f"(lgkmcnt(0)): the reads ahead are lost ({lines[start][:60]})")
+
+
+_M0 = re.compile(r"\bm0\b")
+_M0_COPY = re.compile(r"^s_add_u32 m0, s\d+, 0x[0-9a-f]+$|^s_add_u32 m0, s\d+, \d+$")
+
+
+def check_m0_only_in_copies(text: str, src: str) -> None:
+    """Fail if anything but the wide kernel's own chunk copies touches M0.
+    Each copy sets M0 (its LDS address) inside the same assembly block as its
+    LDS-direct load and lists M0 as clobbered; the compiler treats M0 as
+    reserved, and does not promise to keep a value of its own in M0 across
+    such a block, so the copies are only safe while the compiler uses M0 for
+    nothing else in these kernels."""
+    bad = []
+    for line in text.split("\n"):
+        code = line.split(";", 1)[0].strip()
+        if code and not code.startswith(".") and _M0.search(code) and not _M0_COPY.match(code):
+            bad.append(code)
+    if bad:
+        raise RuntimeError(f"{src}: M0 is used outside the chunk copies: {bad[:4]}")
 
 
 def check_no_scratch(text: str, src: str) -> None:

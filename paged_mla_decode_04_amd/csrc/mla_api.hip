@@ -97,6 +97,17 @@ mla_status check_plan_args(int32_t batch, int32_t q_rows, int32_t h_kv, int32_t 
   return MLA_OK;
 }
 
+// The 128-row decode kernel of a bf16 cache has an instance that plans in
+// its prologue (every wave scans the lengths; the split counts are listed in
+// LDS), used for at most kPlanInKernelMaxBatch sequences and when the plan's
+// costs, with lengths clamped to the table's width, sum below 2^31.  (Built
+// with the plan code, the 16-row kernel ran 20% slower even when given a
+// plan, and the fp8 one spilled registers; they keep the plan kernel.)
+bool plan_fits_kernel(int64_t batch, int c, int64_t max_blocks) {
+  const int64_t units = c + (max_blocks > 1 ? max_blocks : 1);
+  return batch >= 1 && batch <= mla::kPlanInKernelMaxBatch && batch * units < ((int64_t)1 << 31);
+}
+
 // Checks, plan and launches of one decode call.  With no_alloc the plan and the
 // partials go to the static scratch instead of the caller's workspace (whose
 // fields are then ignored).
@@ -162,14 +173,22 @@ mla_status decode_call(const mla_decode_params* p, void* stream, bool no_alloc) 
   hipStream_t s = (hipStream_t)stream;
   const int32_t* tile_md = p->tile_md;
   const int32_t* num_splits = p->num_splits;
+  // No metadata: the decode workgroups plan their own parts when the batch is
+  // small enough for every wave to scan the lengths; otherwise the plan
+  // kernel runs first.  Either way the plan lands in the workspace.
+  const int plan_c = mla::segment_cost(mla::rows_per_block((int)rows));
+  int32_t* plan_md = (int32_t*)(ws + w.tile_md);
+  int32_t* plan_ns = (int32_t*)(ws + w.num_splits);
+  const bool plan_in_kernel = !tile_md && !kv8 && mla::rows_per_block((int)rows) == mla::kRowsPerWorkgroup &&
+                              plan_fits_kernel(p->batch, plan_c, p->max_blocks_per_seq);
   if (!tile_md) {
-    if (p->batch > mla::kMaxPlanBatch) return MLA_ERR_UNSUPPORTED;
-    int32_t* md = (int32_t*)(ws + w.tile_md);
-    int32_t* ns = (int32_t*)(ws + w.num_splits);
-    if (mla::launch_plan(p->cache_seqlens, p->batch, (int)rows, num_parts, md, ns, s) != hipSuccess)
-      return MLA_ERR_HIP;
-    tile_md = md;
-    num_splits = ns;
+    if (!plan_in_kernel) {
+      if (p->batch > mla::kMaxPlanBatch) return MLA_ERR_UNSUPPORTED;
+      if (mla::launch_plan(p->cache_seqlens, p->batch, (int)rows, num_parts, plan_md, plan_ns, s) != hipSuccess)
+        return MLA_ERR_HIP;
+    }
+    tile_md = plan_md;
+    num_splits = plan_ns;
   }
 
   mla::DecodeArgs a;
@@ -197,6 +216,10 @@ mla_status decode_call(const mla_decode_params* p, void* stream, bool no_alloc) 
   a.tile_md = tile_md;
   a.num_splits = num_splits;
   a.num_parts = num_parts;
+  a.plan_in_kernel = plan_in_kernel ? 1 : 0;
+  a.plan_c = plan_c;
+  a.plan_md = plan_in_kernel ? plan_md : nullptr;
+  a.plan_ns = plan_in_kernel ? plan_ns : nullptr;
   a.row_blocks = mla::row_blocks((int)rows);
   a.part_lse = (float*)(ws + w.part_lse);
   a.part_o = (float*)(ws + w.part_o);

@@ -389,14 +389,20 @@ __device__ __forceinline__ Chunk batch_get(const i32x4& b, int i) {
 }
 
 
-template <bool KV8>
+// PLAN: the instance that derives its part from the lengths (no metadata
+// given; bf16 cache only, the fp8 instance has no registers to spare).  The
+// plan code changes the register allocation of the whole kernel, so the
+// instance given a plan is built without it.
+template <bool KV8, bool PLAN>
 __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a) {
+  static_assert(!(KV8 && PLAN), "the fp8 instance takes a plan");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[KV8 ? kSmem8 : kSmemW];
+  __shared__ int32_t split_tab[PLAN ? kPlanInKernelMaxBatch + 1 : 1];  // in-kernel plan: num_splits
   constexpr int kCopies = KV8 ? kCopies8 : kCopiesW;
   const int w = uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   PartInfo pi;
-  if (!load_part(a, kRowsW, pi)) return;
+  if (!load_part<PLAN>(a, kRowsW, pi, (lds_i32*)split_tab)) return;
 
   lds_u8* const lds = (lds_u8*)smem;
   const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
@@ -832,9 +838,10 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
       // the values enter a new segment / close one
       if (D0.valid() && D0.first) {
         const int split = D0.seq == pi.seq_begin ? pi.split_first : 0;
-        const int s0 = ((cint32*)a.num_splits)[D0.seq];
+        int s0, nsplit;
+        segment_splits<PLAN>(a, D0.seq, (const lds_i32*)split_tab, s0, nsplit);
         seg_slot = s0 + split;
-        seg_nsplit = ((cint32*)a.num_splits)[D0.seq + 1] - s0;
+        seg_nsplit = nsplit;
         seg_bad = false;
       }
       if (D0.valid()) {
@@ -928,9 +935,11 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
 hipError_t launch_decode_wide(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)(a.num_parts * a.row_blocks));
   if (a.kv8)
-    hipLaunchKernelGGL(decode_wide_kernel<true>, grid, dim3(kThreadsW), 0, stream, a);
+    hipLaunchKernelGGL((decode_wide_kernel<true, false>), grid, dim3(kThreadsW), 0, stream, a);
+  else if (a.plan_in_kernel)
+    hipLaunchKernelGGL((decode_wide_kernel<false, true>), grid, dim3(kThreadsW), 0, stream, a);
   else
-    hipLaunchKernelGGL(decode_wide_kernel<false>, grid, dim3(kThreadsW), 0, stream, a);
+    hipLaunchKernelGGL((decode_wide_kernel<false, false>), grid, dim3(kThreadsW), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -178,25 +178,182 @@ struct PartInfo {
   int blk_row0;
 };
 
+// ---- The plan inside the decode kernels, used when the caller passes no
+// metadata (at most kPlanInKernelMaxBatch sequences).  It is the plan of
+// mla_plan.h (plan_part, plan_touches), with lengths past the block table's
+// width counted as clamped.  Every wave loads the lengths once (four per
+// lane) and:
+//   * sums the sequence costs c + pages for the stride T;
+//   * scans them into the prefix sums and finds the sequences holding the
+//     part's first unit x = p T and its end x + T (plan_part's searches);
+//   * scans touches(j) = floor((prefix[j+1] - 1) / T) - floor((prefix[j] + c)
+//     / T) + 1 into num_splits.  Wave 0 lists num_splits in LDS (the segment
+//     bookkeeping reads it there) and, in row block 0, publishes for the merge
+//     each sequence's split count from the part that holds its last unit,
+//     which is the last part touching it.
+// The host checks that the costs sum below 2^31, so 32-bit arithmetic holds.
+
+// Inclusive prefix sum over the wave's 64 lanes with DPP moves (no LDS round
+// trips): shifts right by 1, 2, 4 and 8 lanes inside each row of 16 (lanes
+// shifted in from outside the row read 0), then row 0's total added to row 1
+// and row 2's to row 3 (row_bcast:15), then lane 31's total to rows 2 and 3
+// (row_bcast:31).  All lanes must be active.
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+  int x = (int)v;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  return (uint32_t)x;
+}
+__device__ __forceinline__ uint32_t lane_value(uint32_t v, int k) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, k);
+}
+
+// Part `part` from the lengths: fills pi's plan fields; wave 0 fills
+// split_tab[j] = num_splits[j] for every sequence j <= batch.  Row block 0's
+// wave 0 also writes the part's record to plan_md and the split counts it
+// owns to plan_ns.  Returns false for an idle part.
+__device__ __forceinline__ bool plan_in_kernel(const DecodeArgs& a, int part, int mblock, PartInfo& pi,
+                                               lds_i32* split_tab) {
+  constexpr int kBlocks = (kPlanInKernelMaxBatch + 63) / 64;
+  const int lane = threadIdx.x & 63;
+  const int B = a.batch, c = a.plan_c;
+  const bool wave0 = (threadIdx.x >> 6) == 0;
+  const bool writer = mblock == 0 && wave0;
+  const int cap = a.max_blocks * kPageTokens;
+  uint32_t u[kBlocks];
+#pragma unroll
+  for (int k = 0; k < kBlocks; ++k) {
+    const int i = 64 * k + lane;
+    int n = i < B ? a.seqlens[i] : 0;
+    n = n > cap ? cap : n;
+    u[k] = i < B ? (uint32_t)(c + seq_units(n)) : 0u;
+  }
+  uint32_t acc = 0;
+#pragma unroll
+  for (int k = 0; k < kBlocks; ++k) acc += u[k];
+  const uint32_t W = lane_value(wave_incl_scan_u32(acc), 63);
+  const uint32_t T = (uint32_t)plan_stride((int64_t)W, a.num_parts, c);
+  const int64_t x = (int64_t)part * T, xn = x + T;
+  int32_t* md = a.plan_md + (int64_t)part * kTileMdInts;
+  if (x >= (int64_t)W) {
+    if (writer && lane < kTileMdInts) md[lane] = lane == 0 || lane == 2 ? B : 0;
+    return false;
+  }
+  uint32_t carry = 0, pre_b = 0, pre_nb = 0, u_nbm1 = 0, u_last = 0;
+  int b = 0, nb = 0, ns_carry = 0;
+#pragma unroll
+  for (int k = 0; k < kBlocks; ++k) {
+    if (64 * k < B) {
+      const int i = 64 * k + lane;
+      const bool in = i < B;
+      const uint32_t incl = carry + wave_incl_scan_u32(u[k]);  // prefix[i + 1]
+      const uint32_t excl = incl - u[k];                       // prefix[i]
+      const uint64_t hx = __ballot(in && (int64_t)excl <= x && x < (int64_t)incl);
+      const uint64_t hn = __ballot(in && (int64_t)excl <= xn && xn < (int64_t)incl);
+      if (hx) {
+        const int h = __ffsll((unsigned long long)hx) - 1;
+        b = 64 * k + h;
+        pre_b = lane_value(excl, h);
+      }
+      if (hn) {
+        const int h = __ffsll((unsigned long long)hn) - 1;
+        nb = 64 * k + h;
+        pre_nb = lane_value(excl, h);
+        u_nbm1 = h > 0 ? lane_value(u[k], h - 1) : u_last;
+      }
+      const int last = B - 1 - 64 * k < 63 ? B - 1 - 64 * k : 63;
+      u_last = lane_value(u[k], last);
+      carry = lane_value(incl, last);
+      if (wave0) {
+        const int last_part = in ? (int)((incl - 1u) / T) : 0;
+        const int touch = in ? last_part - (int)((excl + (uint32_t)c) / T) + 1 : 0;
+        const int ns_incl = ns_carry + (int)wave_incl_scan_u32((uint32_t)touch);  // num_splits[i + 1]
+        if (in) {
+          split_tab[i] = ns_incl - touch;
+          if (i == B - 1) split_tab[B] = ns_incl;
+          if (writer && last_part == part) a.plan_ns[i + 1] = ns_incl;
+        }
+        ns_carry = (int)lane_value((uint32_t)ns_incl, last);
+      }
+    }
+  }
+  const int64_t off = x - (int64_t)pre_b - c;
+  const int pg = off > 0 ? (int)off : 0;
+  int eb, epg;
+  if (xn >= (int64_t)W) {
+    eb = B - 1;
+    epg = (int)u_last - c;
+  } else {
+    const int64_t noff = xn - (int64_t)pre_nb - c;
+    if (noff > 0) {
+      eb = nb;
+      epg = (int)noff;
+    } else {
+      eb = nb - 1;
+      epg = (int)u_nbm1 - c;
+    }
+  }
+  pi.seq_begin = b;
+  pi.page_begin = pg;
+  pi.seq_last = eb;
+  pi.page_end = epg;
+  pi.split_first = pg > 0 ? part - (int)((pre_b + (uint32_t)c) / T) : 0;
+  if (writer && lane < kTileMdInts) {
+    const int v = lane == 0 ? b : lane == 1 ? pg : lane == 2 ? eb : lane == 3 ? epg : lane == 4 ? pi.split_first : 0;
+    md[lane] = v;
+  }
+  if (writer && part == 0 && lane == 0) a.plan_ns[0] = 0;
+  return true;
+}
+
 // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a contiguous
 // run of (part, row block) pairs so that the row blocks of one part, and
-// neighbouring parts of one sequence, share that XCD's L2.  Returns false
-// for an idle part.
-__device__ __forceinline__ bool load_part(const DecodeArgs& a, int rows_per_block, PartInfo& pi) {
+// neighbouring parts of one sequence, share that XCD's L2.  The part's record
+// comes from the plan's metadata, or from the lengths in a kernel instance
+// that plans (kPlan; then wave 0 also fills split_tab, read after the
+// prologue's barrier).  Returns false for an idle part.
+template <bool kPlan>
+__device__ __forceinline__ bool load_part(const DecodeArgs& a, int rows_per_block, PartInfo& pi, lds_i32* split_tab) {
   const int G = gridDim.x, hw = blockIdx.x;
   const int xcd = hw & 7, pos = hw >> 3;
   const int logical = xcd * (G >> 3) + min(xcd, G & 7) + pos;
   const int part = logical / a.row_blocks;
   const int mblock = logical - part * a.row_blocks;
-  cint32* md = (cint32*)a.tile_md + (int64_t)part * kTileMdInts;
-  pi.seq_begin = md[0];
-  if (pi.seq_begin >= a.batch) return false;
-  pi.page_begin = md[1];
-  pi.seq_last = md[2];
-  pi.page_end = md[3];
-  pi.split_first = md[4];
-  pi.blk_row0 = mblock * rows_per_block;
-  return true;
+  if constexpr (kPlan) {
+    pi.blk_row0 = mblock * rows_per_block;
+    return plan_in_kernel(a, part, mblock, pi, split_tab);
+  } else {
+    cint32* md = (cint32*)a.tile_md + (int64_t)part * kTileMdInts;
+    pi.seq_begin = md[0];
+    if (pi.seq_begin >= a.batch) return false;
+    pi.page_begin = md[1];
+    pi.seq_last = md[2];
+    pi.page_end = md[3];
+    pi.split_first = md[4];
+    pi.blk_row0 = mblock * rows_per_block;
+    return true;
+  }
+}
+
+// A segment of sequence s of the part starts: the first partial slot of s
+// and the number of parts that touch it, from the plan's num_splits or, when
+// the kernel plans, from its copy in LDS.
+template <bool kPlan>
+__device__ __forceinline__ void segment_splits(const DecodeArgs& a, int s, const lds_i32* split_tab, int& slot0,
+                                               int& nsplit) {
+  if constexpr (kPlan) {
+    const int s0 = uniform(split_tab[s]);
+    slot0 = s0;
+    nsplit = uniform(split_tab[s + 1]) - s0;
+  } else {
+    const int s0 = ((cint32*)a.num_splits)[s];
+    slot0 = s0;
+    nsplit = ((cint32*)a.num_splits)[s + 1] - s0;
+  }
 }
 
 }  // namespace mla

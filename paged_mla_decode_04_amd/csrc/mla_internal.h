@@ -20,7 +20,7 @@ struct DecodeArgs {
   int32_t kv8;                 // the cache holds E4M3 bytes (the wide kernel converts them to bf16)
   float kv_scale;              // value of a cache element per unit of its stored number (1 for bf16)
   const int32_t* tile_md;
-  const int32_t* num_splits;
+  const int32_t* num_splits;   // read by the merge (and by the decode unless it plans)
   int32_t num_parts, row_blocks;
   float* part_lse;             // [slots][rows]
   float* part_o;               // narrow kernel: fp32 [slots][rows][512]; wide kernel: fp16 tiles (below)
@@ -29,6 +29,12 @@ struct DecodeArgs {
   int64_t o_sb, o_ss, o_sh;
   float* lse;
   int64_t l_sb, l_ss, l_sh;
+  // No metadata given: each decode workgroup derives its part from the
+  // lengths (plan cost c per sequence), writes its record to plan_md and the
+  // split counts it owns to plan_ns (== num_splits, for the merge).
+  int32_t plan_in_kernel, plan_c;
+  int32_t* plan_md;
+  int32_t* plan_ns;
 };
 
 // Wide kernel partials: per slot, ceil(rows / 32) tiles of 32 rows x 512

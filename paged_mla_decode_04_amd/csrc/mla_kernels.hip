@@ -431,9 +431,10 @@ __device__ __forceinline__ void decode_role(const DecodeArgs& a, const PartInfo&
       }
       if (D0.valid() && D0.first) {  // the values enter a new segment
         const int split = D0.seq == pi.seq_begin ? pi.split_first : 0;
-        const int s0 = ((cint32*)a.num_splits)[D0.seq];
+        int s0, nsplit;
+        segment_splits<false>(a, D0.seq, nullptr, s0, nsplit);
         seg_slot = s0 + split;
-        seg_nsplit = ((cint32*)a.num_splits)[D0.seq + 1] - s0;
+        seg_nsplit = nsplit;
         seg_bad = false;
       }
       if (D0.valid()) seg_bad |= D0.bad;
@@ -528,7 +529,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
 
   PartInfo pi;
-  if (!load_part(a, NRT * 16, pi)) return;
+  if (!load_part<false>(a, NRT * 16, pi, nullptr)) return;
   lds_u8* const lds = (lds_u8*)smem;
   if (wave < 4)
     decode_role<NRT, true>(a, pi, lds, wave, lane);

@@ -42,6 +42,7 @@ constexpr int kPageTokens = 64;
 constexpr int kTileMdInts = 8;
 constexpr int kRowsPerWorkgroup = 128;
 constexpr int kMaxPlanBatch = 16384;  // device plan keeps the prefix sums in LDS
+constexpr int kPlanInKernelMaxBatch = 256;  // the 128-row decode plans for itself up to this batch
 
 // Rows one workgroup handles when the kv head has `rows` query rows: 16, 32
 // or 64 (the narrow kernel, up to 4 score tiles of 16 rows), else 128 (the

@@ -42,8 +42,9 @@ def trace_phases(path: str) -> dict:
     rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
     out: dict = defaultdict(lambda: defaultdict(list))
     seen_flush = False
-    flushed = False       # a flush since the last decode-call kernel
+    flushed = False       # a flush since the last step started
     phase = "warmup"
+    prev = ""             # the previous kernel of a step
     for r in rows:
         name = r["Kernel_Name"]
         dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
@@ -53,12 +54,16 @@ def trace_phases(path: str) -> dict:
             continue
         if not any(k in name for k in DECODE):
             continue
-        if "plan_kernel" in name:  # a step starts with its plan
+        # a step starts with its plan kernel, or with its decode kernel when
+        # the decode plans for itself (no plan kernel right before it)
+        starts = "plan_kernel" in name or ("combine" not in name and "plan_kernel" not in prev)
+        if starts:
             if flushed:
                 phase = "cold"
             elif seen_flush:
                 phase = "warm"
             flushed = False
+        prev = name
         k = short_name(name)
         out[k]["all"].append(dur)
         out[k][phase].append(dur)
@@ -79,10 +84,10 @@ def trace_table(path: str) -> str:
         c = d["cold"]
         lines.append(f"| `{k}` | {len(d['all'])} | {_avg(c):.1f} | {min(c) if c else float('nan'):.1f} | "
                      f"{max(c) if c else float('nan'):.1f} | {_avg(d['warm']):.1f} | {_avg(d['all']):.1f} |")
-    cold_call = sum(_avg(ph[k]["cold"]) for k in ph if "plan_kernel" not in k)
-    warm_call = sum(_avg(ph[k]["warm"]) for k in ph if "plan_kernel" not in k)
+    cold_call = sum(_avg(ph[k]["cold"]) for k in ph)
+    warm_call = sum(_avg(ph[k]["warm"]) for k in ph)
     lines.append("")
-    lines.append(f"Decode call (decode + merge kernels, summed averages): cold {cold_call:.1f} us, "
+    lines.append(f"One step (the kernels above, summed averages): cold {cold_call:.1f} us, "
                  f"warm {warm_call:.1f} us.")
     return "\n".join(lines)
 

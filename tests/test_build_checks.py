@@ -132,3 +132,20 @@ def test_full_lds_waits_in_the_score_loop_are_caught():
 
 def test_the_wide_kernel_keeps_its_score_reads_ahead():
     build.check_fixed_agprs("mla_decode_wide.hip")
+
+
+# ---- M0 belongs to the wide kernel's chunk copies
+
+COPY = ("\ts_add_u32 m0, s12, 0x3c00\n\ts_nop 0\n"
+        "\tbuffer_load_dwordx4 v2, s[8:11], 0 offen offset:128 lds\n")
+
+
+def test_copies_alone_pass_the_m0_ownership_check():
+    build.check_m0_only_in_copies(COPY * 3, "k")
+
+
+def test_a_compiler_use_of_m0_is_caught():
+    for extra in ("\ts_mov_b32 m0, s4\n", "\tv_movrels_b32_e32 v1, v2\n\ts_mov_b32 m0, -1\n",
+                  "\tds_read_b32 v1, v0\n\ts_add_u32 m0, s1, s2\n"):
+        with pytest.raises(RuntimeError, match="M0 is used outside"):
+            build.check_m0_only_in_copies(COPY + extra + COPY, "k")

@@ -25,7 +25,7 @@ import torch
 from conftest import bits
 from oracle import mla_ref
 from paged_mla_decode_04_amd import (get_mla_metadata, mla_decode_with_kvcache, plan_host,
-                                     default_num_parts)
+                                     default_num_parts, workspace_size)
 from paged_mla_decode_04_amd.workloads import D_V, FP8_KV_SCALE, WORKLOADS, Workload, draw
 
 pytestmark = pytest.mark.gpu
@@ -171,6 +171,70 @@ def test_internal_plan_equals_explicit_plan():
     a = run_gpu(inp, num_parts=5, use_metadata=False)
     b = run_gpu(inp, num_parts=5, use_metadata=True)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def plan_in_workspace(ws, parts, batch):
+    """The plan a decode without metadata leaves at the start of its workspace:
+    tile_md [parts][8] at byte 0, num_splits [batch + 1] from the next 256-byte
+    boundary."""
+    md = ws[: parts * 32].view(torch.int32).reshape(parts, 8).cpu()
+    off = (parts * 32 + 255) // 256 * 256
+    return md, ws[off: off + 4 * (batch + 1)].view(torch.int32).cpu()
+
+
+def decode_planning_in_kernel(inp, parts, dev="cuda:0"):
+    """Decode without metadata into a poisoned workspace; returns (out, lse,
+    the plan found in the workspace)."""
+    g = inp.to(dev)
+    w = inp.workload
+    ws = torch.full((workspace_size(w.batch, w.s_q, w.h_q, 1, D_V, parts),), 0xA5, dtype=torch.uint8,
+                    device=dev)
+    out, lse = mla_decode_with_kvcache(g.q, g.blocked_k, g.block_table, g.cache_seqlens, D_V,
+                                       w.softmax_scale, w.causal, num_parts=parts, workspace=ws)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu(), plan_in_workspace(ws, parts, w.batch)
+
+
+def mixed_lengths(batch, seed):
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, 3000, size=batch)
+    lens[rng.random(batch) < 0.2] = 0
+    return tuple(int(x) for x in lens)
+
+
+IN_KERNEL_PLAN_CASES = [
+    ("tiny", None), ("tiny", 1), ("tiny", 5), ("v2lite", None), ("v2lite", 1024), ("skewed", None),
+    ("wide", None), ("wide", 7), ("mtp", None),
+    (Workload("mixed256", batch=256, s_q=1, h_q=32, causal=False, seqlens="fixed",
+              fixed_seqlens=mixed_lengths(256, 3)), 97),
+    (Workload("mixed128", batch=128, s_q=1, h_q=128, causal=False, seqlens="fixed",
+              fixed_seqlens=mixed_lengths(128, 4)), 300),
+    # 257 sequences: past the in-kernel limit, the plan kernel runs first
+    (Workload("mixed257", batch=257, s_q=1, h_q=16, causal=False, seqlens="fixed",
+              fixed_seqlens=mixed_lengths(257, 5)), 64),
+]
+
+
+@pytest.mark.parametrize("case", IN_KERNEL_PLAN_CASES,
+                         ids=[f"{c[0] if isinstance(c[0], str) else c[0].name}-{c[1]}" for c in IN_KERNEL_PLAN_CASES])
+def test_plan_without_metadata_equals_the_host_plan(case):
+    """A decode called without metadata plans inside its kernel (128-row
+    blocks, bf16 cache, up to 256 sequences) or runs the plan kernel first:
+    either way the plan it leaves in the workspace is the host plan, and its
+    results are bit for bit those of a decode given the plan kernel's
+    metadata."""
+    name, parts = case
+    inp = draw(name, seed=7)
+    w = inp.workload
+    rows = w.s_q * w.h_q
+    parts = parts or default_num_parts(rows)
+    note(f"[plan] {w.name} parts={parts}")
+    out, lse, (md, ns) = decode_planning_in_kernel(inp, parts)
+    hmd, hns = plan_host(inp.cache_seqlens, rows, 1, parts)
+    assert torch.equal(md, hmd), f"{w.name}: part records differ"
+    assert torch.equal(ns, hns), f"{w.name}: num_splits differ"
+    out2, lse2, _ = run_gpu(inp, num_parts=parts, use_metadata=True)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2), f"{w.name}: results differ"
 
 
 def test_device_plan_equals_host_plan():
@@ -337,6 +401,14 @@ def test_lengths_past_the_table_are_clamped(h_q, parts):
     note(f"[parity] clamped lengths h_q={h_q} parts={parts}")
     out, lse, _ = run_gpu(inp, num_parts=parts)
     assert_parity(out, lse, ref_out, ref_lse, what=f"clamp h_q={h_q} parts={parts}")
+    # without metadata: the 128-row kernel plans for itself and counts the
+    # clamped lengths; the 16-row one runs the plan kernel on the stored ones
+    note(f"[parity] clamped lengths, no metadata, h_q={h_q} parts={parts}")
+    out, lse, (md, ns) = decode_planning_in_kernel(inp, parts)
+    assert_parity(out, lse, ref_out, ref_lse, what=f"clamp, no metadata, h_q={h_q} parts={parts}")
+    planned = [128, 100, 128] if h_q == 128 else [1000, 100, 129]
+    hmd, hns = plan_host(torch.tensor(planned, dtype=torch.int32), h_q, 1, parts)
+    assert torch.equal(md, hmd) and torch.equal(ns, hns)
 
 
 @pytest.mark.parametrize("h_q,kv", [(128, "bf16"), (16, "bf16"), (128, "fp8_e4m3")])

@@ -136,3 +136,88 @@ def test_plan_rejects_bad_arguments():
         plan_host([1, 2], 16, 1, 0)
     with pytest.raises(ValueError):
         plan_host([1, 2], 4096, 1, 4)
+
+
+# ---- the plan the decode kernels derive for themselves (no metadata passed)
+#
+# Each wave finds its part from two passes over the lengths, 64 at a time,
+# and starts the split bookkeeping from closed forms instead of the full
+# scan of touch counts.  This restates that procedure in Python and checks it
+# against the host mirror: the part records, num_splits at each part's first
+# sequence, and the per-part lists (and which part publishes each entry).
+
+def in_kernel_part(seqlens, c, P, p):
+    """One wave's part record and (prefix, num_splits) at its first sequence."""
+    B = len(seqlens)
+    u = [c + units(n) for n in seqlens]
+    W = sum(u)
+    T = max(c + 1, -(-W // P))
+    x, xn = p * T, p * T + T
+    if x >= W:
+        return [B, 0, B, 0, 0, 0, 0, 0], None
+    carry, b, nb, K, u_prev_last = 0, None, None, 0, None
+    for base in range(0, B, 64):
+        lanes = range(base, min(B, base + 64))
+        excl = {}
+        for i in lanes:
+            excl[i] = carry
+            carry += u[i]
+        # sequences j >= 1 whose window [prefix[j], prefix[j] + c] holds a multiple of T
+        window = [i for i in lanes if i >= 1 and (excl[i] % T == 0 or excl[i] % T >= T - c)]
+        hx = [i for i in lanes if excl[i] <= x < excl[i] + u[i]]
+        if b is None:
+            if hx:
+                b, pre_b = hx[0], excl[hx[0]]
+                K += sum(1 for i in window if i < b)
+            else:
+                K += len(window)
+        hn = [i for i in lanes if excl[i] <= xn < excl[i] + u[i]]
+        if hn:
+            nb, pre_nb = hn[0], excl[hn[0]]
+            u_nbm1 = u[nb - 1] if nb - 1 >= base else u_prev_last
+        u_prev_last = u[lanes[-1]]
+    pg = max(0, x - pre_b - c)
+    if xn >= W:
+        eb, epg = B - 1, u[B - 1] - c
+    elif xn - pre_nb - c > 0:
+        eb, epg = nb, xn - pre_nb - c
+    else:
+        eb, epg = nb - 1, u_nbm1 - c
+    first = p - (pre_b + c) // T if pg > 0 else 0
+    ns_b = 0 if b == 0 else b + (pre_b - 1) // T - K
+    return [b, pg, eb, epg, first, 0, 0, 0], (pre_b, ns_b, T)
+
+
+@pytest.mark.parametrize("seed", range(300))
+def test_in_kernel_plan_closed_forms_match_the_host_plan(seed):
+    rng = random.Random(1000 + seed)
+    b = rng.choice([1, 2, 3, 16, 63, 64, 65, 128, 129, 256])
+    pick = rng.random()
+    if pick < 0.3:
+        seqlens = [rng.randint(0, 200) for _ in range(b)]
+    elif pick < 0.6:
+        seqlens = [rng.randint(0, 9000) for _ in range(b)]
+    else:
+        seqlens = [rng.choice([0, 1, 63, 64, 65, 4096, 32768]) for _ in range(b)]
+    q_rows = rng.choice([16, 32, 128, 256])
+    parts = rng.choice([1, 2, 7, 64, 256, 1024])
+    c = seg_cost(q_rows)
+    md, ns = plan_host(torch.tensor(seqlens, dtype=torch.int32), q_rows, 1, parts)
+    md, ns = md.tolist(), ns.tolist()
+    published = [0] + [None] * b
+    for p in range(parts):
+        rec, start = in_kernel_part(seqlens, c, parts, p)
+        assert rec == md[p], (p, rec, md[p])
+        if start is None:
+            continue
+        pre, nsc, T = start
+        assert nsc == ns[rec[0]]
+        for s in range(rec[0], rec[2] + 1):  # the part's list, built forward
+            nxt = pre + c + units(seqlens[s])
+            touch = (nxt - 1) // T - (pre + c) // T + 1
+            assert (nsc, nsc + touch) == (ns[s], ns[s + 1])
+            if (nxt - 1) // T == p:  # the part holding s's last unit publishes it
+                assert published[s + 1] is None
+                published[s + 1] = nsc + touch
+            pre, nsc = nxt, nsc + touch
+    assert published == ns
