@@ -266,13 +266,17 @@ def main():
             if flush is not None:
                 flush.sum()  # reads 512 MB: L2 and MALL then hold clean lines of another buffer
             e0.record()
-            if graph is not None:  # plan and decode in one replay (e1 marks nothing)
-                e1.record()
+            if graph is not None:  # plan and decode in one replay
+                ev[i] = (e0, e0, e2)
                 graph.replay()
                 e2.record()
                 continue
-            meta = plan()
-            e1.record()
+            if args.separate_plan:
+                meta = plan()
+                e1.record()
+            else:  # the step is the decode call (events recorded twice in a row read ~5 us apart)
+                meta = None
+                ev[i] = (e0, e0, e2)
             decode(meta)
             e2.record()
         torch.cuda.synchronize()
