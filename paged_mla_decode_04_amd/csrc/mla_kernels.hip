@@ -625,19 +625,22 @@ __global__ __launch_bounds__(256) void combine_tiles_kernel(DecodeArgs a) {
 }
 
 // Many splits per sequence (a few long sequences over many parts): workgroup
-// (ct, rt, b) merges column tile ct (32 columns) of row tile rt (32 rows) of
-// sequence b.  Wave v folds splits v, v + 4, ... online, eight splits' loads
-// at a time; the four waves' running sums are then combined through LDS and
-// written as 32 rows of 64 contiguous bytes, lse by column tile 0.  The
-// sequence is the grid's slowest index, so a sequence's workgroups are
-// dispatched together: with more workgroups than fit at once, a long
-// sequence's (the ones that run longest) then do not wait behind other
-// sequences' tiles.
+// (hc, rt, b) merges half hc & 1 (16 columns) of column tile hc >> 1 of row
+// tile rt (32 rows) of sequence b; a half is one 1 KB block of a partial tile
+// (element pair gp of the accumulator layout).  Wave v folds splits v, v + 4,
+// ... online, eight splits' loads at a time; the four waves' running sums are
+// then combined through LDS and written as 32 rows of 32 contiguous bytes,
+// lse by half 0.  Half tiles spread a long sequence's bytes over twice as
+// many compute units as whole tiles would.  The sequence is the grid's
+// slowest index, so a sequence's workgroups are dispatched together: with
+// more workgroups than fit at once, a long sequence's (the ones that run
+// longest) then do not wait behind other sequences' tiles.
 __global__ __launch_bounds__(256) void combine_splits_kernel(DecodeArgs a) {
   __shared__ float red_m[4][64], red_s[4][64];
   __shared__ int red_nan[4][64];
-  __shared__ float red[4][64][16];
-  const int ct = blockIdx.x, rt = blockIdx.y, b = blockIdx.z;
+  __shared__ float red[4][64][8];
+  const int hc = blockIdx.x, rt = blockIdx.y, b = blockIdx.z;
+  const int ct = hc >> 1, gp = hc & 1;
   const int v = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int base = a.num_splits[b];
   const int ns = a.num_splits[b + 1] - base;
@@ -649,14 +652,14 @@ __global__ __launch_bounds__(256) void combine_splits_kernel(DecodeArgs a) {
     const float* lse_p = a.part_lse + (int64_t)base * a.rows + 32 * rt + j;
     const float* scale_p = a.part_scale + (int64_t)base * a.rows + 32 * rt + j;
     const uint8_t* src0 = (const uint8_t*)a.part_o + (int64_t)base * partial_slot_bytes(a.rows) +
-                          (int64_t)rt * kPartialTileBytes + 2048 * ct + 16 * lane;
-    float acc[16];
+                          (int64_t)rt * kPartialTileBytes + 2048 * ct + 1024 * gp + 16 * lane;
+    float acc[8];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
     OnlineLse ol;
     for (int i0 = v; i0 < ns; i0 += 4 * kSplitMergeBatch) {
       float x[kSplitMergeBatch], sc[kSplitMergeBatch];
-      f16x8 d[kSplitMergeBatch][2];
+      f16x8 d[kSplitMergeBatch];
 #pragma unroll
       for (int u = 0; u < kSplitMergeBatch; ++u) {
         const int i = i0 + 4 * u;
@@ -664,32 +667,28 @@ __global__ __launch_bounds__(256) void combine_splits_kernel(DecodeArgs a) {
         x[u] = (in && ok) ? lse_p[(int64_t)i * a.rows] : -INFINITY;
         sc[u] = (in && ok) ? scale_p[(int64_t)i * a.rows] : 0.f;
         const uint8_t* src = src0 + (int64_t)(in ? i : 0) * partial_slot_bytes(a.rows);
-        d[u][0] = in ? *(const f16x8*)src : f16x8{};
-        d[u][1] = in ? *(const f16x8*)(src + 1024) : f16x8{};
+        d[u] = in ? *(const f16x8*)src : f16x8{};
       }
       const float f = ol.fold(x);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[e] *= f;
+      for (int e = 0; e < 8; ++e) acc[e] *= f;
 #pragma unroll
       for (int u = 0; u < kSplitMergeBatch; ++u) {
         const float wgt = x[u] * sc[u];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          acc[e] += wgt * (float)d[u][0][e];
-          acc[8 + e] += wgt * (float)d[u][1][e];
-        }
+        for (int e = 0; e < 8; ++e) acc[e] += wgt * (float)d[u][e];
       }
     }
     red_m[v][lane] = ol.m;
     red_s[v][lane] = ol.sum;
     red_nan[v][lane] = ol.nan;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) red[v][lane][e] = acc[e];
+    for (int e = 0; e < 8; ++e) red[v][lane][e] = acc[e];
   }
   __syncthreads();
   {
-    // row j = t / 8, output columns 4 c .. 4 c + 3 of the tile; column i of
-    // the tile is accumulator 4 (i / 8) + i % 4 of lane j + 32 ((i / 4) % 2)
+    // row j = t / 8, output columns 2 c, 2 c + 1 of the half; column i of the
+    // half is accumulator 4 (i / 8) + i % 4 of lane j + 32 ((i / 4) % 2)
     const int j = t >> 3, c = t & 7;
     const int row = 32 * rt + j;
     float M = -INFINITY;
@@ -707,19 +706,19 @@ __global__ __launch_bounds__(256) void combine_splits_kernel(DecodeArgs a) {
     }
     const float inv = nan ? __builtin_nanf("") : (S > 0.f ? 1.f / S : 0.f);
     const float L = nan ? __builtin_nanf("") : (M == -INFINITY ? -INFINITY : M + __builtin_amdgcn_logf(S) * kLn2);
-    bf16x4 o4;
+    bf16x2 o2;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 4 * c + e;
+    for (int e = 0; e < 2; ++e) {
+      const int i = 2 * c + e;
       const int ln = j + 32 * ((i >> 2) & 1), r = 4 * (i >> 3) + (i & 3);
       const float val = wv[0] * red[0][ln][r] + wv[1] * red[1][ln][r] + wv[2] * red[2][ln][r] + wv[3] * red[3][ln][r];
-      o4[e] = (__bf16)(val * inv);
+      o2[e] = (__bf16)(val * inv);
     }
     if (row < a.rows) {
       const int qi = row / a.h_q, hh = row - qi * a.h_q;
-      uint16_t* op = a.out + (int64_t)b * a.o_sb + (int64_t)qi * a.o_ss + (int64_t)hh * a.o_sh + 32 * ct + 4 * c;
-      *(bf16x4*)op = o4;
-      if (ct == 0 && c == 0) a.lse[(int64_t)b * a.l_sb + (int64_t)qi * a.l_ss + (int64_t)hh * a.l_sh] = L;
+      uint16_t* op = a.out + (int64_t)b * a.o_sb + (int64_t)qi * a.o_ss + (int64_t)hh * a.o_sh + 32 * ct + 16 * gp + 2 * c;
+      *(bf16x2*)op = o2;
+      if (hc == 0 && c == 0) a.lse[(int64_t)b * a.l_sb + (int64_t)qi * a.l_ss + (int64_t)hh * a.l_sh] = L;
     }
   }
 }
@@ -803,7 +802,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream) {
   if (rows_per_block(a.rows) == kRowsPerWorkgroup || a.kv8) {
     if (many_splits(a.num_parts, a.batch)) {
-      const dim3 grid((unsigned)(kDv / 32), (unsigned)((a.rows + 31) / 32), (unsigned)a.batch);
+      const dim3 grid((unsigned)(kDv / 16), (unsigned)((a.rows + 31) / 32), (unsigned)a.batch);
       hipLaunchKernelGGL(combine_splits_kernel, grid, dim3(256), 0, stream, a);
     } else {
       const dim3 grid((unsigned)a.batch, (unsigned)((a.rows + 31) / 32));
