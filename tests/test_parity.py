@@ -205,13 +205,16 @@ def mixed_lengths(batch, seed):
 IN_KERNEL_PLAN_CASES = [
     ("tiny", None), ("tiny", 1), ("tiny", 5), ("v2lite", None), ("v2lite", 1024), ("skewed", None),
     ("wide", None), ("wide", 7), ("mtp", None),
-    (Workload("mixed256", batch=256, s_q=1, h_q=32, causal=False, seqlens="fixed",
+    # 256 sequences: the in-kernel limit, four full blocks of 64 lengths per wave
+    (Workload("mixed256", batch=256, s_q=1, h_q=128, causal=False, seqlens="fixed",
               fixed_seqlens=mixed_lengths(256, 3)), 97),
     (Workload("mixed128", batch=128, s_q=1, h_q=128, causal=False, seqlens="fixed",
               fixed_seqlens=mixed_lengths(128, 4)), 300),
     # 257 sequences: past the in-kernel limit, the plan kernel runs first
-    (Workload("mixed257", batch=257, s_q=1, h_q=16, causal=False, seqlens="fixed",
+    (Workload("mixed257", batch=257, s_q=1, h_q=128, causal=False, seqlens="fixed",
               fixed_seqlens=mixed_lengths(257, 5)), 64),
+    (Workload("mixed40", batch=40, s_q=1, h_q=32, causal=False, seqlens="fixed",
+              fixed_seqlens=mixed_lengths(40, 6)), 23),
 ]
 
 
