@@ -307,12 +307,17 @@ struct BatchPos {
   bool more;       // the part has chunks from there on
 };
 
-__device__ __forceinline__ i32x4 desc_batch(const DecodeArgs& a, const PartInfo& pi, BatchPos& pos, int lane) {
+// The lengths a batch from pos may need: lane k holds that of sequence
+// pos.seq + k (0 past the part's last sequence).
+__device__ __forceinline__ int batch_lengths(const DecodeArgs& a, const PartInfo& pi, const BatchPos& pos, int lane) {
+  const int sk = pos.seq + lane;
+  return sk <= pi.seq_last ? clamp_len(a, a.seqlens[sk]) : 0;
+}
+
+// nk: batch_lengths(pos), however obtained.
+__device__ __forceinline__ i32x4 desc_batch(const DecodeArgs& a, const PartInfo& pi, BatchPos& pos, int lane, int nk) {
   i32x4 out = i32x4{-1, 0, 0, -1};
   if (!pos.more) return out;
-  // lengths of the sequences the batch may touch: lane k holds sequence pos.seq + k
-  const int sk = pos.seq + lane;
-  const int nk = sk <= pi.seq_last ? clamp_len(a, a.seqlens[sk]) : 0;
   int rem = lane;  // chunks still to skip before this lane's own
   bool found = false;
   int my_seq = -1, my_chunk = 0, my_n = 0, my_lo = 0, my_hi = 0;
@@ -402,7 +407,8 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
   const int w = uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   PartInfo pi;
-  if (!load_part<PLAN>(a, kRowsW, pi, (lds_i32*)split_tab)) return;
+  int plan_len[kPlanBlocks];  // the in-kernel plan's lengths (PLAN)
+  if (!load_part<PLAN>(a, kRowsW, pi, (lds_i32*)split_tab, plan_len)) return;
 
   lds_u8* const lds = (lds_u8*)smem;
   const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
@@ -752,50 +758,39 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
     asm volatile("s_nop 4" ::: "memory");
   };
 
-  // ---- prologue.  The first sequence's queries need only the part record,
-  // so they go out first (all parts start at once, and the queries are most
-  // of the bytes every part needs before its first step).  The copies of the
-  // part's first two chunks need the first sequence's length and the table
-  // entry of its first page (scalar loads issued with the queries), and go
-  // out before the lane-parallel descriptor batch is built (its two dependent
-  // loads then overlap the copies).  A first segment of one chunk copies its
-  // second chunk from the batch instead.  With an fp8 cache: chunks 0 and 1
-  // copied to staging, chunk 0 converted to its bf16 slot, chunk 2 copied (it
-  // lands during step -1, which converts chunk 1).
+  // ---- prologue.  The descriptor batch comes first: its loads (the lengths,
+  // unless the plan already holds them, then the block-table entries) would
+  // otherwise complete only after everything issued before them.  Then the
+  // copies of the part's first two chunks, then the first sequence's queries
+  // (most of the bytes a part needs before its first step, and all parts
+  // start at once).  With an fp8 cache: chunks 0 and 1 copied to staging,
+  // chunk 0 converted to its bf16 slot, chunk 2 copied (it lands during step
+  // -1, which converts chunk 1).
   const int seq0 = pi.seq_begin;
-  load_queries(Chunk{seq0, 0, 0, 0, false, false, false});
-  const int n0 = clamp_len(a, load_len(a, seq0));
-  const int phys0 = load_phys(a, seq0, pi.page_begin);
-  auto early_chunk = [&](int chunk) -> Chunk {
-    int tok = n0 - kChunk * chunk;
-    tok = tok < 0 ? 0 : (tok > kChunk ? kChunk : tok);
-    const bool bad = tok > 0 && !(phys0 >= 0 && phys0 < a.num_blocks);
-    return Chunk{seq0, chunk, tok, phys0, false, false, bad};
-  };
-  // (the same range rule as the batch walk: the part's end, one chunk at least)
-  int hi0 = chunk_count(n0);
-  if (seq0 == pi.seq_last && 2 * pi.page_end < hi0) hi0 = 2 * pi.page_end;
-  if (hi0 <= 2 * pi.page_begin) hi0 = 2 * pi.page_begin + 1;
-  const bool second_early = 2 * pi.page_begin + 1 < hi0;
-  const Chunk E1 = early_chunk(2 * pi.page_begin), E2 = early_chunk(2 * pi.page_begin + 1);
-  const uint32_t stage_base = (uint32_t)kSlots8 * kTileBytes;
-  const uint32_t first_dst = KV8 ? lds_addr + stage_base : lds_addr;
-  const uint32_t second_dst = KV8 ? lds_addr + stage_base + kStageBytes : lds_addr + kTileBytes;
-  copy_chunk(E1, first_dst);
-  if (second_early) copy_chunk(E2, second_dst);
-
   BatchPos bpos;
-  bpos.seq = pi.seq_begin;
+  bpos.seq = seq0;
   bpos.chunk = 2 * pi.page_begin;
   bpos.more = true;
-  i32x4 batch = desc_batch(a, pi, bpos, lane);
+  int nk0;
+  if constexpr (PLAN) {
+    // (a cross-lane read: every lane takes part, whatever it keeps)
+    const int sk = seq0 + lane;
+    const int n = planned_length(plan_len, sk);
+    nk0 = sk <= pi.seq_last ? clamp_len(a, n) : 0;
+  } else {
+    nk0 = batch_lengths(a, pi, bpos, lane);
+  }
+  i32x4 batch = desc_batch(a, pi, bpos, lane, nk0);
   int c0 = 0;  // chunk ordinal of the batch's first descriptor
   Chunk D0 = unpack_chunk(i32x4{-1, 0, 0, -1});  // chunk t: values
   Chunk D1 = batch_get(batch, 0);                // chunk t + 1: scores
   Chunk D2 = batch_get(batch, 1);                // chunk t + 2: landing (fp8: converted this step)
   Chunk D3 = batch_get(batch, 2);                // chunk t + 3: copied this step (fp8: in flight)
   Chunk D4 = KV8 ? batch_get(batch, 3) : D3;     // fp8: chunk t + 4, copied this step
-  if (!second_early) copy_chunk(D2, second_dst);
+  const uint32_t stage_base = (uint32_t)kSlots8 * kTileBytes;
+  copy_chunk(D1, KV8 ? lds_addr + stage_base : lds_addr);
+  copy_chunk(D2, KV8 ? lds_addr + stage_base + kStageBytes : lds_addr + kTileBytes);
+  load_queries(Chunk{seq0, 0, 0, 0, false, false, false});
   // fp8: bf16 slots of chunks t, t + 1, t + 2 (rotating) and the staging
   // slot of chunks t + 2 and t + 4 (alternating with that of t + 3)
   uint32_t bs0 = 2 * kTileBytes, bs1 = 0, bs2 = kTileBytes;
@@ -920,7 +915,7 @@ __global__ __launch_bounds__(kThreadsW, 1) void decode_wide_kernel(DecodeArgs a)
     // the descriptor of the chunk copied next step (a new batch every 64 chunks)
     constexpr int kAhead = KV8 ? 5 : 4;
     if (t + kAhead - c0 >= 64) {
-      batch = desc_batch(a, pi, bpos, lane);
+      batch = desc_batch(a, pi, bpos, lane, batch_lengths(a, pi, bpos, lane));
       c0 += 64;
     }
     if constexpr (KV8)

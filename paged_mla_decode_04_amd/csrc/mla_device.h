@@ -213,25 +213,30 @@ __device__ __forceinline__ uint32_t lane_value(uint32_t v, int k) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, k);
 }
 
-// Part `part` from the lengths: fills pi's plan fields; wave 0 fills
-// split_tab[j] = num_splits[j] for every sequence j <= batch.  Row block 0's
-// wave 0 also writes the part's record to plan_md and the split counts it
-// owns to plan_ns.  Returns false for an idle part.
+// Part `part` from the lengths: fills pi's plan fields and len (lane l of
+// len[k]: the stored length of sequence 64 k + l); wave 0 fills split_tab[j] =
+// num_splits[j] for every sequence j <= batch.  Row block 0's wave 0 also
+// writes the part's record to plan_md and the split counts it owns to
+// plan_ns.  Returns false for an idle part.
+constexpr int kPlanBlocks = (kPlanInKernelMaxBatch + 63) / 64;  // lengths per lane
+
 __device__ __forceinline__ bool plan_in_kernel(const DecodeArgs& a, int part, int mblock, PartInfo& pi,
-                                               lds_i32* split_tab) {
-  constexpr int kBlocks = (kPlanInKernelMaxBatch + 63) / 64;
+                                               lds_i32* split_tab, int (&len)[kPlanBlocks]) {
+  constexpr int kBlocks = kPlanBlocks;
   const int lane = threadIdx.x & 63;
   const int B = a.batch, c = a.plan_c;
   const bool wave0 = (threadIdx.x >> 6) == 0;
   const bool writer = mblock == 0 && wave0;
   const int cap = a.max_blocks * kPageTokens;
+  // the lengths, four per lane, loaded together (an index past the batch
+  // reads the last length again and counts nothing), with one wait
+#pragma unroll
+  for (int k = 0; k < kBlocks; ++k) len[k] = a.seqlens[64 * k + lane < B ? 64 * k + lane : B - 1];
   uint32_t u[kBlocks];
 #pragma unroll
   for (int k = 0; k < kBlocks; ++k) {
-    const int i = 64 * k + lane;
-    int n = i < B ? a.seqlens[i] : 0;
-    n = n > cap ? cap : n;
-    u[k] = i < B ? (uint32_t)(c + seq_units(n)) : 0u;
+    const int n = len[k] > cap ? cap : len[k];
+    u[k] = 64 * k + lane < B ? (uint32_t)(c + seq_units(n)) : 0u;
   }
   uint32_t acc = 0;
 #pragma unroll
@@ -316,9 +321,11 @@ __device__ __forceinline__ bool plan_in_kernel(const DecodeArgs& a, int part, in
 // neighbouring parts of one sequence, share that XCD's L2.  The part's record
 // comes from the plan's metadata, or from the lengths in a kernel instance
 // that plans (kPlan; then wave 0 also fills split_tab, read after the
-// prologue's barrier).  Returns false for an idle part.
+// prologue's barrier, and len holds the lengths).  Returns false for an idle
+// part.
 template <bool kPlan>
-__device__ __forceinline__ bool load_part(const DecodeArgs& a, int rows_per_block, PartInfo& pi, lds_i32* split_tab) {
+__device__ __forceinline__ bool load_part(const DecodeArgs& a, int rows_per_block, PartInfo& pi, lds_i32* split_tab,
+                                          int (&len)[kPlanBlocks]) {
   const int G = gridDim.x, hw = blockIdx.x;
   const int xcd = hw & 7, pos = hw >> 3;
   const int logical = xcd * (G >> 3) + min(xcd, G & 7) + pos;
@@ -326,7 +333,7 @@ __device__ __forceinline__ bool load_part(const DecodeArgs& a, int rows_per_bloc
   const int mblock = logical - part * a.row_blocks;
   if constexpr (kPlan) {
     pi.blk_row0 = mblock * rows_per_block;
-    return plan_in_kernel(a, part, mblock, pi, split_tab);
+    return plan_in_kernel(a, part, mblock, pi, split_tab, len);
   } else {
     cint32* md = (cint32*)a.tile_md + (int64_t)part * kTileMdInts;
     pi.seq_begin = md[0];
@@ -338,6 +345,19 @@ __device__ __forceinline__ bool load_part(const DecodeArgs& a, int rows_per_bloc
     pi.blk_row0 = mblock * rows_per_block;
     return true;
   }
+}
+
+// The stored length of sequence s (per lane, 0 <= s < 64 kPlanBlocks) from
+// the lengths the in-kernel plan loaded: lane s % 64 of len[s / 64].  A
+// cross-lane read: call it with every lane of the wave active.
+__device__ __forceinline__ int planned_length(const int (&len)[kPlanBlocks], int s) {
+  int v = 0;
+#pragma unroll
+  for (int k = 0; k < kPlanBlocks; ++k) {
+    const int x = __shfl(len[k], s & 63);
+    v = (s >> 6) == k ? x : v;
+  }
+  return v;
 }
 
 // A segment of sequence s of the part starts: the first partial slot of s

@@ -529,7 +529,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
 
   PartInfo pi;
-  if (!load_part<false>(a, NRT * 16, pi, nullptr)) return;
+  int unused_len[kPlanBlocks];
+  if (!load_part<false>(a, NRT * 16, pi, nullptr, unused_len)) return;
   lds_u8* const lds = (lds_u8*)smem;
   if (wave < 4)
     decode_role<NRT, true>(a, pi, lds, wave, lane);
