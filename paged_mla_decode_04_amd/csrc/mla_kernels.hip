@@ -615,14 +615,15 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   if (lane == 0) a.lse[(int64_t)b * a.l_sb + (int64_t)qi * a.l_ss + (int64_t)h * a.l_sh] = L;
 }
 
-// Few splits per sequence: one workgroup per (sequence, 32-row tile).
+// Few splits per sequence: one workgroup per (sequence, 32-row tile, column
+// half).
 __global__ __launch_bounds__(256) void combine_tiles_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[32 * kMergeTileStride];
-  const int b = blockIdx.x, rt = blockIdx.y;
+  const int b = blockIdx.x, rt = blockIdx.y, hf = blockIdx.z;
   const int base = a.num_splits[b];
   const int ns = a.num_splits[b + 1] - base;
   if (ns <= 1) return;
-  merge_row_tile(a, b, rt, base, ns, (lds_u16*)tile);
+  merge_row_tile(a, b, rt, hf, base, ns, (lds_u16*)tile);
 }
 
 // Many splits per sequence (a few long sequences over many parts): workgroup
@@ -806,7 +807,7 @@ hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream) {
       const dim3 grid((unsigned)(kDv / 16), (unsigned)((a.rows + 31) / 32), (unsigned)a.batch);
       hipLaunchKernelGGL(combine_splits_kernel, grid, dim3(256), 0, stream, a);
     } else {
-      const dim3 grid((unsigned)a.batch, (unsigned)((a.rows + 31) / 32));
+      const dim3 grid((unsigned)a.batch, (unsigned)((a.rows + 31) / 32), 2u);
       hipLaunchKernelGGL(combine_tiles_kernel, grid, dim3(256), 0, stream, a);
     }
     return hipGetLastError();

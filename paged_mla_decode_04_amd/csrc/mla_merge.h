@@ -56,15 +56,17 @@ struct OnlineLse {
 
 constexpr int kTileMergeBatch = 4;    // splits whose loads are in flight together (tile merge)
 constexpr int kSplitMergeBatch = 8;   // ... per wave (split-parallel merge)
-constexpr int kMergeTileStride = kDv + 8;  // bf16 elements per row of the merge's LDS tile
+constexpr int kMergeTileStride = kDv / 2 + 8;  // bf16 elements per row of the merge's LDS half tile
 
 // Merges the ns >= 2 partials in slots base .. base + ns - 1 of row tile rt
-// (32 rows) of sequence b into out and lse, with 256 threads (4 waves).  Wave
-// v merges column tiles 4 v .. 4 v + 3 of the 32 rows in the accumulator
-// layout the partials keep; the tile then goes through LDS (`tile`, 32 rows of
-// kMergeTileStride bf16) so that every output row is written as one 1 KB
-// store.  Ends with a barrier, so the LDS tile may be reused at once.
-__device__ __forceinline__ void merge_row_tile(const DecodeArgs& a, int b, int rt, int base, int ns,
+// (32 rows) of sequence b into out and lse, for column half hf (256 columns,
+// column tiles 8 hf .. 8 hf + 7), with 256 threads (4 waves).  Wave v merges
+// column tiles 8 hf + 2 v and 8 hf + 2 v + 1 of the 32 rows in the
+// accumulator layout the partials keep; the half tile then goes through LDS
+// (`tile`, 32 rows of kMergeTileStride bf16) so that every output row is
+// written as 512 contiguous bytes.  Half 0 writes the lse.  Ends with a
+// barrier, so the LDS tile may be reused at once.
+__device__ __forceinline__ void merge_row_tile(const DecodeArgs& a, int b, int rt, int hf, int base, int ns,
                                                lds_u16* tile) {
   const int v = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j = lane & 31, h = lane >> 5;
@@ -73,16 +75,16 @@ __device__ __forceinline__ void merge_row_tile(const DecodeArgs& a, int b, int r
   const float* lse_p = a.part_lse + (int64_t)base * a.rows + row;
   const float* scale_p = a.part_scale + (int64_t)base * a.rows + row;
   const uint8_t* src0 = (const uint8_t*)a.part_o + (int64_t)base * partial_slot_bytes(a.rows) +
-                        (int64_t)rt * kPartialTileBytes + 8 * 1024 * v + 16 * lane;
-  float acc[8][8];
+                        (int64_t)rt * kPartialTileBytes + 2048 * (8 * hf + 2 * v) + 16 * lane;
+  float acc[4][8];
 #pragma unroll
-  for (int p = 0; p < 8; ++p)
+  for (int p = 0; p < 4; ++p)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[p][e] = 0.f;
   OnlineLse ol;
   for (int i0 = 0; i0 < ns; i0 += kTileMergeBatch) {
     float x[kTileMergeBatch], sc[kTileMergeBatch];
-    f16x8 pv[kTileMergeBatch][8];
+    f16x8 pv[kTileMergeBatch][4];
 #pragma unroll
     for (int u = 0; u < kTileMergeBatch; ++u) {
       const int i = i0 + u;
@@ -91,28 +93,28 @@ __device__ __forceinline__ void merge_row_tile(const DecodeArgs& a, int b, int r
       sc[u] = (in && ok) ? scale_p[(int64_t)i * a.rows] : 0.f;
       const uint8_t* src = src0 + (int64_t)(in ? i : 0) * partial_slot_bytes(a.rows);
 #pragma unroll
-      for (int p = 0; p < 8; ++p) pv[u][p] = in ? *(const f16x8*)(src + 1024 * p) : f16x8{};
+      for (int p = 0; p < 4; ++p) pv[u][p] = in ? *(const f16x8*)(src + 1024 * p) : f16x8{};
     }
     const float f = ol.fold(x);
 #pragma unroll
-    for (int p = 0; p < 8; ++p)
+    for (int p = 0; p < 4; ++p)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[p][e] *= f;
 #pragma unroll
     for (int u = 0; u < kTileMergeBatch; ++u) {
       const float wgt = x[u] * sc[u];
 #pragma unroll
-      for (int p = 0; p < 8; ++p)
+      for (int p = 0; p < 4; ++p)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[p][e] += wgt * (float)pv[u][p][e];
     }
   }
   const float Lo = ol.lse();
   const float inv = (ol.nan || !(ol.sum > 0.f)) ? (ol.nan ? __builtin_nanf("") : 0.f) : 1.f / ol.sum;
-  // pair p of wave v: column tile ct = 4 v + (p >> 1), elements of g = 2 (p & 1) + (e >> 2)
+  // pair p of wave v: column tile 2 v + (p >> 1) of the half, elements of g = 2 (p & 1) + (e >> 2)
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const int ct = 4 * v + (p >> 1);
+  for (int p = 0; p < 4; ++p) {
+    const int ct = 2 * v + (p >> 1);
 #pragma unroll
     for (int gg = 0; gg < 2; ++gg) {
       const int col = 32 * ct + 8 * (2 * (p & 1) + gg) + 4 * h;
@@ -122,19 +124,19 @@ __device__ __forceinline__ void merge_row_tile(const DecodeArgs& a, int b, int r
       *(__attribute__((address_space(3))) bf16x4*)(tile + j * kMergeTileStride + col) = o4;
     }
   }
-  if (v == 0 && h == 0 && ok) {
+  if (hf == 0 && v == 0 && h == 0 && ok) {
     const int qi = row / a.h_q, hh = row - qi * a.h_q;
     a.lse[(int64_t)b * a.l_sb + (int64_t)qi * a.l_ss + (int64_t)hh * a.l_sh] = Lo;
   }
   __syncthreads();
-  // wave v writes rows 8 v .. 8 v + 7, 64 lanes x 16 bytes each
+  // wave v writes rows 8 v .. 8 v + 7, two at a time: 32 lanes x 16 bytes each
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const int jr = 8 * v + r, orow = 32 * rt + jr;
+  for (int r = 0; r < 8; r += 2) {
+    const int jr = 8 * v + r + h, orow = 32 * rt + jr;
     if (orow < a.rows) {
       const int qi = orow / a.h_q, hh = orow - qi * a.h_q;
-      uint16_t* op = a.out + (int64_t)b * a.o_sb + (int64_t)qi * a.o_ss + (int64_t)hh * a.o_sh + 8 * lane;
-      *(bf16x8*)op = *(const lds_bf16x8*)(tile + jr * kMergeTileStride + 8 * lane);
+      uint16_t* op = a.out + (int64_t)b * a.o_sb + (int64_t)qi * a.o_ss + (int64_t)hh * a.o_sh + 256 * hf + 8 * j;
+      *(bf16x8*)op = *(const lds_bf16x8*)(tile + jr * kMergeTileStride + 8 * j);
     }
   }
   __syncthreads();
