@@ -301,6 +301,8 @@ def check_lds_dma(src: str) -> None:
         if r.returncode != 0:
             raise RuntimeError(f"hipcc -S failed for {src}:\n" + r.stdout.decode(errors="replace"))
         check_lds_dma_m0_hazards(out, src)
+        with open(out) as f:
+            check_no_scratch(f.read(), src)
 
 
 def build(verbose: bool = False) -> str:

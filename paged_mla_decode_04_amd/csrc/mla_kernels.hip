@@ -192,7 +192,7 @@ __device__ __forceinline__ void decode_role(const DecodeArgs& a, const PartInfo&
   };
 
   // ---- prologue: wave 4 publishes chunks 0..4; copies of chunks 0, 1 and 2;
-  // queries of the first segment
+  // queries of the first segment (with one row tile, loaded during the walk)
   Cursor cur, nxt;  // producer: the next chunk to publish and the one after
   bool prod_first = false;
   if (producer) {
@@ -212,6 +212,11 @@ __device__ __forceinline__ void decode_role(const DecodeArgs& a, const PartInfo&
     }
     nxt = next_chunk(a, cur, pi.seq_last, pi.page_end);
   }
+  // the first segment's queries need only the part record: the score waves
+  // load them while the producer walks (with one row tile; with more, the
+  // registers they hold across the copies' address work spill)
+  constexpr bool kEarlyQueries = SCORE && NRT == 1;
+  if constexpr (kEarlyQueries) load_queries(Chunk{pi.seq_begin, 0, 0, 0, false, false, false});
   block_sync();
   Chunk D0 = unpack_chunk(i32x4{-1, 0, 0, -1});  // chunk t (values)
   Chunk D1 = unpack_chunk(ring[0]);              // chunk t + 1 (scores)
@@ -221,7 +226,7 @@ __device__ __forceinline__ void decode_role(const DecodeArgs& a, const PartInfo&
   issue_copy<SCORE>(a, D1, lds_addr, wave, lane);
   issue_copy<SCORE>(a, D2, lds_addr + kChunkBytes, wave, lane);
   issue_copy<SCORE>(a, D3, lds_addr + 2 * kChunkBytes, wave, lane);
-  if constexpr (SCORE) load_queries(D1);
+  if constexpr (SCORE && !kEarlyQueries) load_queries(D1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   block_sync();
   bool p_last = false;  // chunk t - 1 ended its segment (the values still have to close it)
