@@ -543,11 +543,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     decode_role<NRT, false>(a, pi, lds, wave, lane);
 }
 
-constexpr int kMergeUnroll = 4;  // splits whose loads are in flight together
+constexpr int kMergeUnroll = 8;  // splits whose loads are in flight together
 
 // Merge the partials of every sequence that more than one part touched:
 // L = log(sum_i exp(lse_i)), out = sum_i exp(lse_i - L) * O_i (empty partials,
-// lse = -inf, weigh nothing; all empty gives out = 0, lse = -inf).
+// lse = -inf, weigh nothing; all empty gives out = 0, lse = -inf; a NaN lse
+// gives NaN).  One wave per (sequence, row), in one online pass over the
+// splits (OnlineLse), eight splits' loads at a time.
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int b = blockIdx.x;
   const int r = blockIdx.y * 4 + (threadIdx.x >> 6);
@@ -556,66 +558,43 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int ns = a.num_splits[b + 1] - base;
   if (ns <= 1 || r >= a.rows) return;
   const float* lse_p = a.part_lse + (int64_t)base * a.rows + r;
-  // L in one pass (online max and sum), four loads in flight
-  float mx = -INFINITY, sum = 0.f;
-  bool nan = false;
+  const f32x4* src0 = (const f32x4*)(a.part_o + ((int64_t)base * a.rows + r) * kDv + 8 * lane);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  OnlineLse ol;
   for (int i0 = 0; i0 < ns; i0 += kMergeUnroll) {
     float x[kMergeUnroll];
-#pragma unroll
-    for (int u = 0; u < kMergeUnroll; ++u) x[u] = i0 + u < ns ? lse_p[(int64_t)(i0 + u) * a.rows] : -INFINITY;
+    f32x4 v0[kMergeUnroll], v1[kMergeUnroll];
 #pragma unroll
     for (int u = 0; u < kMergeUnroll; ++u) {
-      if (x[u] != x[u]) {
-        nan = true;
-      } else if (x[u] > mx) {
-        sum = sum * __builtin_amdgcn_exp2f((mx - x[u]) * kLog2e) + 1.f;
-        mx = x[u];
-      } else if (x[u] != -INFINITY) {
-        sum += __builtin_amdgcn_exp2f((x[u] - mx) * kLog2e);
+      if (i0 + u < ns) {
+        x[u] = lse_p[(int64_t)(i0 + u) * a.rows];
+        const f32x4* src = src0 + (int64_t)(i0 + u) * a.rows * (kDv / 4);
+        v0[u] = src[0];
+        v1[u] = src[1];
+      } else {
+        x[u] = -INFINITY;
+        v0[u] = v1[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    const float f = ol.fold(x);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] *= f;
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[j] += x[u] * v0[u][j];
+        acc[4 + j] += x[u] * v1[u][j];
       }
     }
   }
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float L = -INFINITY;
-  if (mx != -INFINITY && !nan) {
-    L = mx + __builtin_amdgcn_logf(sum) * kLn2;
-    const f32x4* src0 = (const f32x4*)(a.part_o + ((int64_t)base * a.rows + r) * kDv + 8 * lane);
-    for (int i0 = 0; i0 < ns; i0 += kMergeUnroll) {
-      float x[kMergeUnroll];
-      f32x4 v0[kMergeUnroll], v1[kMergeUnroll];
-#pragma unroll
-      for (int u = 0; u < kMergeUnroll; ++u) {
-        if (i0 + u < ns) {
-          x[u] = lse_p[(int64_t)(i0 + u) * a.rows];
-          const f32x4* src = src0 + (int64_t)(i0 + u) * a.rows * (kDv / 4);
-          v0[u] = src[0];
-          v1[u] = src[1];
-        } else {
-          x[u] = -INFINITY;
-          v0[u] = v1[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kMergeUnroll; ++u) {
-        const float w = __builtin_amdgcn_exp2f((x[u] - L) * kLog2e);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc[j] += w * v0[u][j];
-          acc[4 + j] += w * v1[u][j];
-        }
-      }
-    }
-  }
-  if (nan) {
-    L = __builtin_nanf("");
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = __builtin_nanf("");
-  }
+  const float L = ol.lse();
+  const float inv = ol.nan ? __builtin_nanf("") : (ol.sum > 0.f ? 1.f / ol.sum : 0.f);
   const int qi = r / a.h_q, h = r - qi * a.h_q;
   uint16_t* op = a.out + (int64_t)b * a.o_sb + (int64_t)qi * a.o_ss + (int64_t)h * a.o_sh + 8 * lane;
   bf16x8 w;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) w[j] = (__bf16)acc[j];
+  for (int j = 0; j < 8; ++j) w[j] = (__bf16)(acc[j] * inv);
   *(bf16x8*)op = w;
   if (lane == 0) a.lse[(int64_t)b * a.l_sb + (int64_t)qi * a.l_ss + (int64_t)h * a.l_sh] = L;
 }

@@ -1,7 +1,6 @@
-// The merge of a split sequence's partial results by their log-sum-exp, for
-// the wide kernel's fp16 tile partials: shared by the tile merge kernel and
-// by the decode kernel's own merge (the last piece of a sequence to finish
-// merges all of them).
+// The merge of a split sequence's partial results by their log-sum-exp:
+// the online fold all three merge kernels use, and the row-tile merge of the
+// wide kernel's fp16 tile partials.
 //
 // Flash-Decoding splits the key length of a sequence across workgroups and
 // rescales the pieces by their log-sum-exp when it combines them (Hacker News
