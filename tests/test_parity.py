@@ -215,6 +215,11 @@ IN_KERNEL_PLAN_CASES = [
               fixed_seqlens=mixed_lengths(257, 5)), 64),
     (Workload("mixed40", batch=40, s_q=1, h_q=32, causal=False, seqlens="fixed",
               fixed_seqlens=mixed_lengths(40, 6)), 23),
+    # most parts idle (13 cost units over 64 parts), and a single sequence
+    (Workload("idle", batch=3, s_q=1, h_q=128, causal=False, seqlens="fixed",
+              fixed_seqlens=(5, 70, 1)), 64),
+    (Workload("one", batch=1, s_q=2, h_q=128, causal=True, seqlens="fixed",
+              fixed_seqlens=(700,)), 16),
 ]
 
 
