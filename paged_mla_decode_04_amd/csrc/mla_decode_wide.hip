@@ -97,7 +97,7 @@ template <int Q, uint32_t LSTRIDE = 4096u>
 __device__ __forceinline__ void copy_block(__amdgpu_buffer_rsrc_t rsrc, uint32_t lane_off, uint32_t wave_base) {
   // (M0 = wave_base + the block's constant, written here: the compiler would
   // otherwise keep nine such sums in scalar registers, spilled under pressure)
-  asm volatile("s_add_u32 m0, %3, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen offset:%2 lds" ::"v"(lane_off),
+  asm volatile("s_add_u32 m0, %3, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen offset:%2 nt lds" ::"v"(lane_off),
                "s"(rsrc), "n"(128 * Q), "s"(wave_base), "n"((LSTRIDE - 128u) * Q)
                : "memory", "m0", "scc");
 }

@@ -73,7 +73,7 @@ typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
 // that write, which the compiler's hazard check does not see through inline
 // assembly, so the s_nop is part of the block.
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr)
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr)
                : "memory");
 }
 // Position of the page-bookkeeping cursor: one 32-token chunk of the part's
