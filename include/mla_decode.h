@@ -155,11 +155,10 @@ typedef struct mla_decode_params {
      NULL tile_md: the call plans internally with num_parts parts (num_parts <= 0: the
      device default), and the workspace then starts with that plan: tile_md
      [num_parts][MLA_TILE_MD_INTS] at byte 0, num_splits [batch + 1] at the next 256-byte
-     boundary.  For a bf16 cache with at most 256 sequences (and a row block of other than
-     64 rows, i.e. s_q * h_q / h_kv not in 33..64) the decode kernels plan for themselves in
-     their first instructions instead of after a separate plan launch; their plan is
-     mla_get_metadata's except that lengths past max_blocks_per_seq * 64 count as that
-     many tokens. */
+     boundary.  For a bf16 cache with more than 64 query rows per kv head (s_q * h_q /
+     h_kv > 64) and at most 256 sequences, the decode kernel plans for itself in its first
+     instructions instead of after a separate plan launch; its plan is mla_get_metadata's
+     except that lengths past max_blocks_per_seq * 64 count as that many tokens. */
   const int32_t* tile_md;
   const int32_t* num_splits;
   int32_t num_parts;

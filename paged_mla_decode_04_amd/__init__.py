@@ -104,8 +104,9 @@ def mla_decode_with_kvcache(q: torch.Tensor, blocked_k: torch.Tensor, block_tabl
     block_table int32 [b, max_blocks_per_seq]
     cache_seqlens int32 [b]
     metadata    optional (tile_md, num_splits) from get_mla_metadata for these seqlens;
-                without it the call plans for itself (for a bf16 cache of at most 256
-                sequences inside the decode kernels, with no separate plan launch)
+                without it the call plans for itself (inside the decode kernel, with
+                no separate plan launch, for a bf16 cache, more than 64 query rows per
+                kv head and at most 256 sequences)
     no_alloc    use mla_decode_with_kvcache_noalloc: the library's static scratch
                 instead of a workspace (none is allocated; `workspace` is ignored)
     Returns (out bf16 [b, s_q, h_q, dv], lse fp32 [b, s_q, h_q]).
